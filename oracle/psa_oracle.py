@@ -1,0 +1,351 @@
+"""CPU oracle for the Pyramid Sparse Attention (PSA) forward pass.
+
+TEST INFRASTRUCTURE ONLY. Tests, the smoke check and the benchmark's CPU
+baseline may call this module; the product path (the HIP library and its
+Python binding) never does, and this module imports nothing from it.
+
+Plain, slow and float64 throughout. Each function follows one step of the
+method as the pages describe it:
+
+* "PSA: Pyramid Sparse Attention for Efficient Video Understanding and
+  Generation" (chatpaper.ai), abstract: multi-level pooled KV, a level per
+  (query block, KV block) pair, lower levels for critical blocks, pruning.
+* top168.com article on arXiv:2512.04025, paragraph on the pyramid (average
+  pooling, each level coarser) and the paragraph naming the three components
+  (progressive pooling, a multi-level mask generator driven by query-block /
+  KV-block importance, attention that keeps the probability distribution
+  consistent); ablation paragraph (threshold-based assignment).
+* skillmd.com "Psa Pyramid Sparse Attention", sections "Pooled KV cache
+  creation" (pool factor 2**level, average pooling over tokens) and "Block
+  importance scoring" (query against the block's mean key).
+
+Where the pages leave a step open, the reading taken is stated in the
+function's docstring. The precise arithmetic of the probability-consistency
+step (one softmax, each pooled key's logit raised by the log of its pool size)
+is this project's reading of "probability distribution consistency".
+
+Every function here has at least one independent pin in tests/ (closed forms,
+brute force, invariants, a hand-worked example); the comparison with the
+authors' own PSA outputs is "parity unpinned": the pages print no numeric
+example and the authors' code is not available.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+LN2 = math.log(2.0)
+
+
+# ----------------------------------------------------------------------------
+# Rounding to the I/O dtype (the pyramid and O are typed outputs)
+# ----------------------------------------------------------------------------
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even), returned as float64.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range; values below
+    the smallest normal are rounded on the fixed subnormal grid 2**-133."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = (x != 0) & np.isfinite(x)
+    m, e = np.frexp(x[nz])                   # x = m * 2**e, 0.5 <= |m| < 1
+    ulp_exp = np.maximum(e - 8, -133)        # 8 significant bits
+    out[nz] = np.ldexp(np.rint(np.ldexp(x[nz], -ulp_exp)), ulp_exp)   # rint: ties to even
+    out[~nz] = x[~nz]
+    big = np.abs(out) > 3.3895313892515355e38   # largest finite bfloat16
+    out[big] = np.sign(out[big]) * np.inf
+    return out
+
+
+def round_to_io(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# O1: the pyramid
+# ----------------------------------------------------------------------------
+
+def pooled_rows(N: int, level: int) -> int:
+    """Number of pooled rows at ``level``: ceil(N / 2**level)."""
+    return -(-N // (1 << level))
+
+
+def pool_counts(N: int, level: int) -> np.ndarray:
+    """c_l[p] = number of tokens averaged into pooled row p (2**level except a ragged last row)."""
+    P = 1 << level
+    starts = np.arange(pooled_rows(N, level)) * P
+    return (np.minimum(starts + P, N) - starts).astype(np.int64)
+
+
+def pool_level(x: np.ndarray, level: int) -> np.ndarray:
+    """Average pooling over tokens with factor 2**level (skillmd.com, "Pooled KV cache creation").
+
+    x: [..., N, d]. Pooled row p is the mean of tokens [p*2**l, min((p+1)*2**l, N));
+    a ragged last group is averaged over the tokens it has (reading: the pages are
+    silent on it). Level 0 is x itself."""
+    x = np.asarray(x, dtype=np.float64)
+    if level == 0:
+        return x.copy()
+    N = x.shape[-2]
+    P = 1 << level
+    R = pooled_rows(N, level)
+    pad = R * P - N
+    xp = np.concatenate([x, np.zeros(x.shape[:-2] + (pad, x.shape[-1]))], axis=-2) if pad else x
+    sums = xp.reshape(x.shape[:-2] + (R, P, x.shape[-1])).sum(axis=-2)
+    return sums / pool_counts(N, level)[:, None]
+
+
+def build_pyramid(x: np.ndarray, num_levels: int) -> List[np.ndarray]:
+    """[level 0 (x itself), level 1, ..., level L-1] as exact float64 means.
+
+    The article says the levels are built by progressive pooling; in exact
+    arithmetic pooling each level from the one below equals pooling the tokens
+    directly, so the oracle pools directly."""
+    return [pool_level(x, l) for l in range(num_levels)]
+
+
+def pyramid_concat(levels: Sequence[np.ndarray]) -> np.ndarray:
+    """Level-major concatenation of levels 1..L-1 along the token axis ([..., sum_l R_l, d])."""
+    if len(levels) <= 1:
+        shape = levels[0].shape[:-2] + (0, levels[0].shape[-1])
+        return np.zeros(shape)
+    return np.concatenate(list(levels[1:]), axis=-2)
+
+
+def pyramid_row_offsets(N: int, num_levels: int) -> List[int]:
+    """Row offset of level l (l >= 1) in the concatenated pyramid; index 0 unused (0)."""
+    offs = [0, 0]
+    for l in range(1, num_levels):
+        offs.append(offs[-1] + pooled_rows(N, l))
+    return offs[:num_levels]
+
+
+# ----------------------------------------------------------------------------
+# O2: block means
+# ----------------------------------------------------------------------------
+
+def block_sizes(N: int, block: int) -> np.ndarray:
+    """n_j: tokens in block j (block tokens [j*block, min((j+1)*block, N)))."""
+    nb = -(-N // block)
+    starts = np.arange(nb) * block
+    return (np.minimum(starts + block, N) - starts).astype(np.int64)
+
+
+def block_means(x: np.ndarray, block: int) -> np.ndarray:
+    """Mean over the tokens of each block: [..., N, d] -> [..., nblocks, d].
+
+    For keys this is the block's mean key that the scoring step dots the query
+    with (skillmd.com, "Block importance scoring"); for queries it is the mean
+    of the query block (reading: the mask is per query block, abstract)."""
+    x = np.asarray(x, dtype=np.float64)
+    N = x.shape[-2]
+    n = block_sizes(N, block)
+    out = np.empty(x.shape[:-2] + (len(n), x.shape[-1]))
+    for j in range(len(n)):
+        out[..., j, :] = x[..., j * block: j * block + n[j], :].sum(axis=-2) / n[j]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# O3-O5: scores, mass, levels
+# ----------------------------------------------------------------------------
+
+def kv_head_of(h: int, H: int, H_kv: int) -> int:
+    """Query head h reads KV head h // (H / H_kv) (consecutive groups; reading, pages silent)."""
+    return h // (H // H_kv)
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray, n_kv: np.ndarray, scale: float) -> np.ndarray:
+    """z[b,h,i,j] = scale * <qbar[b,h,i], kbar[b,g(h),j]> + ln n_j.
+
+    The dot product is the skillmd.com scoring step (query against the mean key);
+    the + ln n_j term weights a block by its token count the same way the
+    attention step weights a pooled key (equal for all full blocks)."""
+    B, H, nqb, d = qbar.shape
+    H_kv = kbar.shape[1]
+    z = np.empty((B, H, nqb, kbar.shape[2]))
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, H_kv)
+            z[b, h] = scale * (qbar[b, h] @ kbar[b, g].T) + np.log(n_kv.astype(np.float64))[None, :]
+    return z
+
+
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    """p = softmax over the last axis (the KV blocks of one query-block row)."""
+    m = z.max(axis=-1, keepdims=True)
+    e = np.exp(z - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def importance_order(z_row: np.ndarray) -> np.ndarray:
+    """Block indices from most to least important: z descending, ties by index ascending."""
+    j = np.arange(z_row.shape[0])
+    return np.lexsort((j, -z_row))
+
+
+def cumulative_mass(z: np.ndarray, p: np.ndarray) -> np.ndarray:
+    """C[..., j] = total p of the blocks strictly ahead of j in importance order (exclusive)."""
+    C = np.empty_like(p)
+    flat_z = z.reshape(-1, z.shape[-1])
+    flat_p = p.reshape(-1, p.shape[-1])
+    flat_C = C.reshape(-1, p.shape[-1])
+    for r in range(flat_z.shape[0]):
+        order = importance_order(flat_z[r])
+        ps = flat_p[r][order]
+        excl = np.concatenate([[0.0], np.cumsum(ps)[:-1]])
+        flat_C[r, order] = excl
+    return C
+
+
+def assign_levels(C: np.ndarray, thresholds: Sequence[float], num_levels: int,
+                  n_dense_prefix: int = 0, kv_block: int = 64) -> np.ndarray:
+    """level_j = min{l : C_j < tau_l}, or -1 (pruned) if no level qualifies; then every
+    KV block overlapping tokens [0, n_dense_prefix) is set to level 0.
+
+    Thresholds are compared as the float32 numbers the library receives."""
+    tau = np.asarray(thresholds, dtype=np.float32).astype(np.float64)[:num_levels]
+    lev = np.full(C.shape, -1, dtype=np.int8)
+    for l in range(num_levels - 1, -1, -1):
+        lev[C < tau[l]] = l
+    if n_dense_prefix > 0:
+        nforce = -(-n_dense_prefix // kv_block)
+        lev[..., :nforce] = 0
+    return lev
+
+
+def estimate_mask(q: np.ndarray, k: np.ndarray, q_block: int, kv_block: int,
+                  thresholds: Sequence[float], num_levels: int, scale: float,
+                  n_dense_prefix: int = 0) -> Dict[str, np.ndarray]:
+    """The whole mask step: q/k [B,H(_kv),N,d] -> level map [B,H,nqb,nkb] int8 (+ intermediates)."""
+    N = q.shape[-2]
+    qbar = block_means(q, q_block)
+    kbar = block_means(k, kv_block)
+    n_kv = block_sizes(N, kv_block)
+    z = block_scores(qbar, kbar, n_kv, scale)
+    p = softmax_rows(z)
+    C = cumulative_mass(z, p)
+    lev = assign_levels(C, thresholds, num_levels, n_dense_prefix, kv_block)
+    return {"qbar": qbar, "kbar": kbar, "z": z, "p": p, "cmass": C, "levels": lev}
+
+
+# ----------------------------------------------------------------------------
+# O6: pyramid attention under one softmax
+# ----------------------------------------------------------------------------
+
+def gather_keys(levels_row: np.ndarray, N: int, kv_block: int,
+                kpyr: Sequence[np.ndarray], vpyr: Sequence[np.ndarray]):
+    """Keys, values and log pool sizes that one query block attends to.
+
+    KV block j at level l contributes its pooled rows [j*b/2**l, ceil((j*b + n_j)/2**l))
+    of level l (level 0: its tokens). kpyr/vpyr: per-level [N_l, d] arrays."""
+    n_kv = block_sizes(N, kv_block)
+    ks, vs, lc = [], [], []
+    for j, l in enumerate(levels_row):
+        l = int(l)
+        if l < 0:
+            continue
+        P = 1 << l
+        lo = (j * kv_block) // P
+        hi = -(-(j * kv_block + int(n_kv[j])) // P)
+        ks.append(kpyr[l][lo:hi])
+        vs.append(vpyr[l][lo:hi])
+        lc.append(np.log(pool_counts(N, l)[lo:hi].astype(np.float64)))
+    d = kpyr[0].shape[-1]
+    if not ks:
+        return np.zeros((0, d)), np.zeros((0, d)), np.zeros(0)
+    return np.concatenate(ks), np.concatenate(vs), np.concatenate(lc)
+
+
+def attention_rows(qrows: np.ndarray, keys: np.ndarray, vals: np.ndarray, logc: np.ndarray,
+                   scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One softmax over mixed-resolution keys; logit = scale*<q, key> + ln(pool count).
+
+    Two passes (max, then exp and sums). Returns (O [m, d], LSE [m]); a row with no
+    key gives O = 0 and LSE = -inf."""
+    m = qrows.shape[0]
+    if keys.shape[0] == 0:
+        return np.zeros((m, qrows.shape[1])), np.full(m, -np.inf)
+    a = scale * (qrows @ keys.T) + logc[None, :]
+    M = a.max(axis=1, keepdims=True)
+    e = np.exp(a - M)
+    s = e.sum(axis=1, keepdims=True)
+    return (e @ vals) / s, (M + np.log(s))[:, 0]
+
+
+def pyramid_attention(q: np.ndarray, kpyr_levels: Sequence[np.ndarray], vpyr_levels: Sequence[np.ndarray],
+                      level_map: np.ndarray, q_block: int, kv_block: int, scale: float,
+                      items=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Pyramid attention for all (or some) query blocks.
+
+    q [B,H,N,d]; kpyr_levels[l] [B,H_kv,N_l,d] (level 0 = K); level_map [B,H,nqb,nkb].
+    ``items``: optional iterable of (b, h, i) query blocks; other rows of the result are NaN.
+    Returns O [B,H,N,d] and LSE [B,H,N] (float64)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, N, d = q.shape
+    H_kv = kpyr_levels[0].shape[1]
+    nqb = -(-N // q_block)
+    O = np.full((B, H, N, d), np.nan)
+    LSE = np.full((B, H, N), np.nan)
+    if items is None:
+        items = [(b, h, i) for b in range(B) for h in range(H) for i in range(nqb)]
+    for (b, h, i) in items:
+        g = kv_head_of(h, H, H_kv)
+        keys, vals, logc = gather_keys(level_map[b, h, i], N, kv_block,
+                                       [lv[b, g] for lv in kpyr_levels], [lv[b, g] for lv in vpyr_levels])
+        r0, r1 = i * q_block, min((i + 1) * q_block, N)
+        O[b, h, r0:r1], LSE[b, h, r0:r1] = attention_rows(q[b, h, r0:r1], keys, vals, logc, scale)
+    return O, LSE
+
+
+def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Textbook softmax(scale * Q K^T) V per head (KV head g(h) for query head h)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    O = np.empty((B, H, N, d))
+    LSE = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, H_kv)
+            O[b, h], LSE[b, h] = attention_rows(q[b, h], np.asarray(k[b, g], np.float64),
+                                                np.asarray(v[b, g], np.float64), np.zeros(N), scale)
+    return O, LSE
+
+
+# ----------------------------------------------------------------------------
+# Work accounting
+# ----------------------------------------------------------------------------
+
+def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, d: int) -> float:
+    """sum over retained (b,h,i,j) of 4 * m_i * ceil(n_j / 2**l) * d: QK^T and PV on the
+    pooled rows actually attended to (no padding, no exp)."""
+    m = block_sizes(N, q_block).astype(np.float64)
+    n = block_sizes(N, kv_block)
+    lm = level_map.reshape(-1, level_map.shape[-2], level_map.shape[-1])
+    total = 0.0
+    top = int(lm.max()) if lm.size else -1
+    for l in range(top + 1):
+        rows_l = (-(-n // (1 << l))).astype(np.float64)          # pooled rows of each block at level l
+        sel = (lm == l).astype(np.float64)                       # [B*H, nqb, nkb]
+        total += float(np.einsum("xij,i,j->", sel, m, rows_l))
+    return 4.0 * d * total
+
+
+def run_forward(q, k, v, q_block, kv_block, thresholds, num_levels, scale, io_dtype,
+                n_dense_prefix=0, items=None):
+    """All three steps chained: pyramid (rounded to the I/O dtype), mask, attention."""
+    kp = build_pyramid(k, num_levels)
+    vp = build_pyramid(v, num_levels)
+    kp_io = [np.asarray(k, np.float64)] + [round_to_io(x, io_dtype) for x in kp[1:]]
+    vp_io = [np.asarray(v, np.float64)] + [round_to_io(x, io_dtype) for x in vp[1:]]
+    mask = estimate_mask(q, k, q_block, kv_block, thresholds, num_levels, scale, n_dense_prefix)
+    O, LSE = pyramid_attention(q, kp_io, vp_io, mask["levels"], q_block, kv_block, scale, items)
+    return {"kpyr": kp_io, "vpyr": vp_io, "mask": mask, "O": O, "LSE": LSE}

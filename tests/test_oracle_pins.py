@@ -1,0 +1,390 @@
+"""Pins for the CPU oracle: every check here is independent of the oracle's own code
+(closed forms, brute force with explicit loops, invariants the mathematics fixes,
+a hand-derived worked example, library routines for textbook special cases)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import psa_oracle as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------------------- rounding
+
+def test_bf16_rounding_matches_torch_on_float32_values():
+    x = rng(0).standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    x = np.concatenate([x, np.float32([1.0, 65504.0, 1e-30, -7.5e-39, 3.0e38])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = o.round_to_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_rounding_ties_to_even():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: even mantissa is 1.
+    assert o.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6: even is 1 + 2^-6.
+    assert o.round_to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    assert o.round_to_bf16(np.array([1.0 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1.0 + 2.0 ** -7
+
+
+# ----------------------------------------------------------------------------- pyramid (O1)
+
+def brute_pool(x, level):
+    N, d = x.shape
+    P = 2 ** level
+    rows = []
+    for p in range(-(-N // P)):
+        toks = list(range(p * P, min(p * P + P, N)))
+        rows.append([math.fsum(x[t, c] for t in toks) / len(toks) for c in range(d)])
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("N", [64, 130, 2045, 8])
+def test_pool_brute_force(N):
+    x = rng(N).standard_normal((N, 5))
+    for l in range(4):
+        np.testing.assert_allclose(o.pool_level(x, l), brute_pool(x, l), rtol=0, atol=1e-13)
+
+
+def test_pool_constant_and_ramp_closed_forms():
+    N = 2045
+    const = np.full((1, 3, N, 4), 2.75)
+    for lv in o.build_pyramid(const, 4):
+        np.testing.assert_allclose(lv, 2.75, rtol=0, atol=1e-14)
+    a, b = -1.5, 0.25
+    t = np.arange(N, dtype=np.float64)
+    ramp = (a + b * t)[:, None] * np.ones((1, 2))
+    for l in range(4):
+        P = 2 ** l
+        starts = np.arange(-(-N // P)) * P
+        c = np.minimum(starts + P, N) - starts
+        expect = a + b * (starts + (c - 1) / 2.0)
+        np.testing.assert_allclose(o.pool_level(ramp, l)[:, 0], expect, rtol=0, atol=1e-11)
+        np.testing.assert_array_equal(o.pool_counts(N, l), c)
+
+
+def test_progressive_equals_direct():
+    x = rng(5).standard_normal((2, 2045, 3))
+    prev, prev_c = x, np.ones(2045)
+    for l in range(1, 4):
+        R = prev.shape[-2]
+        nxt = []
+        cnt = []
+        for p in range(-(-R // 2)):
+            idx = [r for r in (2 * p, 2 * p + 1) if r < R]
+            w = prev_c[idx]
+            nxt.append(sum(prev[:, r] * prev_c[r] for r in idx) / w.sum())
+            cnt.append(w.sum())
+        prev, prev_c = np.stack(nxt, axis=1), np.array(cnt)
+        np.testing.assert_allclose(o.pool_level(x, l), prev, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(o.pool_counts(2045, l), prev_c)
+
+
+def test_pyramid_layout_offsets():
+    N = 2045
+    x = rng(1).standard_normal((1, 1, N, 2))
+    levels = o.build_pyramid(x, 4)
+    cat = o.pyramid_concat(levels)
+    offs = o.pyramid_row_offsets(N, 4)
+    assert cat.shape[-2] == sum(-(-N // 2 ** l) for l in (1, 2, 3))
+    for l in (1, 2, 3):
+        R = -(-N // 2 ** l)
+        np.testing.assert_array_equal(cat[..., offs[l]:offs[l] + R, :], levels[l])
+
+
+# ----------------------------------------------------------------------------- means, scores (O2, O3)
+
+def test_block_means_brute_force():
+    x = rng(2).standard_normal((130, 3))
+    got = o.block_means(x, 64)
+    for j, (lo, hi) in enumerate([(0, 64), (64, 128), (128, 130)]):
+        for c in range(3):
+            assert abs(got[j, c] - math.fsum(x[lo:hi, c]) / (hi - lo)) < 1e-14
+    np.testing.assert_array_equal(o.block_sizes(130, 64), [64, 64, 2])
+
+
+def test_scores_brute_force_and_softmax_sums_to_one():
+    B, H, Hkv, d = 1, 4, 2, 6
+    qbar = rng(3).standard_normal((B, H, 3, d))
+    kbar = rng(4).standard_normal((B, Hkv, 5, d))
+    n = np.array([64, 64, 64, 64, 7])
+    s = 0.37
+    z = o.block_scores(qbar, kbar, n, s)
+    for h in range(H):
+        g = h // 2
+        for i in range(3):
+            for j in range(5):
+                ref = s * math.fsum(qbar[0, h, i, c] * kbar[0, g, j, c] for c in range(d)) + math.log(n[j])
+                assert abs(z[0, h, i, j] - ref) < 1e-13
+    p = o.softmax_rows(z)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-15)
+    # softmax: ratios are exp of score differences
+    np.testing.assert_allclose(p[..., 1] / p[..., 0], np.exp(z[..., 1] - z[..., 0]), rtol=1e-12)
+
+
+def test_mask_shift_invariance():
+    q = rng(6).standard_normal((1, 2, 256, 8))
+    k = rng(7).standard_normal((1, 2, 256, 8))
+    tau = (0.3, 0.5, 0.7, 0.9)
+    m1 = o.estimate_mask(q, k, 64, 64, tau, 4, 0.35)
+    m2 = o.estimate_mask(q, k + rng(8).standard_normal(8) * 3.0, 64, 64, tau, 4, 0.35)
+    np.testing.assert_allclose(m1["p"], m2["p"], rtol=1e-10, atol=1e-14)
+    np.testing.assert_array_equal(m1["levels"], m2["levels"])
+
+
+# ----------------------------------------------------------------------------- mass and levels (O4, O5)
+
+def brute_cmass(z_row, p_row):
+    n = len(z_row)
+    out = []
+    for j in range(n):
+        ahead = [p_row[k] for k in range(n)
+                 if z_row[k] > z_row[j] or (z_row[k] == z_row[j] and k < j)]
+        out.append(math.fsum(ahead))
+    return np.array(out)
+
+
+def test_cumulative_mass_brute_force_with_ties():
+    z = rng(9).standard_normal((6, 40))
+    z[:, 5] = z[:, 17]          # exact ties, broken by index
+    z[:, 30] = z[:, 2]
+    p = o.softmax_rows(z)
+    C = o.cumulative_mass(z, p)
+    for r in range(6):
+        np.testing.assert_allclose(C[r], brute_cmass(z[r], p[r]), rtol=0, atol=1e-14)
+    # the top block has no mass ahead of it
+    top = np.argmax(z, axis=1)
+    assert np.all(C[np.arange(6), top] == 0.0)
+
+
+def test_levels_brute_force():
+    C = rng(10).uniform(0, 1, size=(3, 50))
+    tau = (0.1, 0.1, 0.45, 0.8)
+    lev = o.assign_levels(C, tau, 4)
+    for idx in np.ndindex(C.shape):
+        ok = [l for l in range(4) if C[idx] < np.float32(tau[l])]
+        assert lev[idx] == (min(ok) if ok else -1)
+    assert not np.any(lev == 1)          # tau_1 == tau_0: level 1 is empty
+
+
+def test_uniform_scores_closed_form():
+    # Q = 0 and N a multiple of the block: every score equals ln 64, p = 1/nkb, ties broken
+    # by index, so C_j = j/nkb and level_j = min{l : j/nkb < tau_l}.
+    N, nkb = 2048, 32
+    q = np.zeros((1, 1, N, 4))
+    k = rng(11).standard_normal((1, 1, N, 4))
+    tau = (0.25, 0.5, 0.625, 0.875)
+    m = o.estimate_mask(q, k, 64, 64, tau, 4, 0.5)
+    j = np.arange(nkb)
+    np.testing.assert_allclose(m["cmass"][0, 0, 0], j / nkb, rtol=0, atol=1e-15)
+    expect = np.array([min([l for l in range(4) if jj / nkb < tau[l]], default=-1) for jj in j])
+    np.testing.assert_array_equal(m["levels"][0, 0, 0], expect)
+    np.testing.assert_array_equal(m["levels"][0, 0, 0][:8], 0)
+    np.testing.assert_array_equal(m["levels"][0, 0, 0][28:], -1)
+
+
+def test_levels_monotone_in_thresholds_and_all_ones():
+    q = rng(12).standard_normal((1, 2, 512, 8))
+    k = rng(13).standard_normal((1, 2, 512, 8))
+    base = np.array([0.2, 0.4, 0.6, 0.8])
+    lev0 = o.estimate_mask(q, k, 64, 64, base, 4, 0.35)["levels"].astype(int)
+    lev0[lev0 < 0] = 99
+    for l in range(4):
+        up = base.copy()
+        up[l:] = np.minimum(up[l:] + 0.15, 1.0)
+        lev1 = o.estimate_mask(q, k, 64, 64, up, 4, 0.35)["levels"].astype(int)
+        lev1[lev1 < 0] = 99
+        assert np.all(lev1 <= lev0)
+    ones = o.estimate_mask(q, k, 64, 64, (1, 1, 1, 1), 4, 0.35)["levels"]
+    assert np.all(ones == 0)
+
+
+def test_dense_prefix_forced_after_ranking():
+    q = rng(14).standard_normal((1, 1, 640, 8))
+    k = rng(15).standard_normal((1, 1, 640, 8))
+    tau = (0.1, 0.2, 0.3, 0.4)
+    plain = o.estimate_mask(q, k, 128, 64, tau, 4, 0.35)
+    forced = o.estimate_mask(q, k, 128, 64, tau, 4, 0.35, n_dense_prefix=130)
+    assert np.all(forced["levels"][..., :3] == 0)
+    np.testing.assert_array_equal(forced["levels"][..., 3:], plain["levels"][..., 3:])
+    np.testing.assert_array_equal(forced["cmass"], plain["cmass"])
+
+
+# ----------------------------------------------------------------------------- attention (O6)
+
+def brute_attention_row(qr, keys, vals, weights_log, scale):
+    a = [scale * math.fsum(qr[c] * key[c] for c in range(len(qr))) + wl for key, wl in zip(keys, weights_log)]
+    M = max(a)
+    e = [math.exp(x - M) for x in a]
+    s = math.fsum(e)
+    out = [math.fsum(e[t] * vals[t][c] for t in range(len(e))) / s for c in range(len(vals[0]))]
+    return np.array(out), M + math.log(s)
+
+
+def small_case(seed, B=1, H=2, Hkv=2, N=256, d=8):
+    r = rng(seed)
+    return (r.standard_normal((B, H, N, d)), r.standard_normal((B, Hkv, N, d)),
+            r.standard_normal((B, Hkv, N, d)))
+
+
+def test_all_level0_equals_dense_brute_force():
+    q, k, v = small_case(20, N=130, d=5)
+    s = 0.41
+    kp, vp = o.build_pyramid(k, 4), o.build_pyramid(v, 4)
+    lev = np.zeros((1, 2, 3, 3), dtype=np.int8)
+    O, L = o.pyramid_attention(q, kp, vp, lev, 64, 64, s)
+    for h in range(2):
+        for r in (0, 63, 64, 129):
+            ref_o, ref_l = brute_attention_row(q[0, h, r], k[0, h], v[0, h], [0.0] * 130, s)
+            np.testing.assert_allclose(O[0, h, r], ref_o, rtol=0, atol=1e-12)
+            assert abs(L[0, h, r] - ref_l) < 1e-12
+    Od, Ld = o.dense_attention(q, k, v, s)
+    np.testing.assert_allclose(O, Od, rtol=0, atol=1e-12)
+
+
+def test_expanded_key_equivalence():
+    # A pooled row of count c acts exactly like c copies of the pooled key/value in dense attention.
+    N = 2045
+    q, k, v = small_case(21, N=N, d=6)
+    s = 0.3
+    kp, vp = o.build_pyramid(k, 4), o.build_pyramid(v, 4)
+    nkb = -(-N // 64)
+    lev = rng(22).integers(-1, 4, size=(1, 2, 16, nkb)).astype(np.int8)
+    lev[..., 0] = 0
+    O, L = o.pyramid_attention(q, kp, vp, lev, 128, 64, s, items=[(0, 1, 3), (0, 0, 15)])
+    for (h, i) in [(1, 3), (0, 15)]:
+        ek, ev = [], []
+        for j in range(nkb):
+            l = int(lev[0, h, i, j])
+            if l < 0:
+                continue
+            P = 2 ** l
+            for t in range(j * 64, min(j * 64 + 64, N)):   # each token contributes its pooled row once
+                ek.append(kp[l][0, h, t // P])
+                ev.append(vp[l][0, h, t // P])
+        for r in (i * 128, min(i * 128 + 127, N - 1)):
+            ref_o, ref_l = brute_attention_row(q[0, h, r], ek, ev, [0.0] * len(ek), s)
+            np.testing.assert_allclose(O[0, h, r], ref_o, rtol=0, atol=1e-11)
+            assert abs(L[0, h, r] - ref_l) < 1e-11
+
+
+def test_identical_keys_block_is_level_invariant():
+    q, k, v = small_case(23, N=512, d=8)
+    k[0, :, 128:192] = k[0, :, 128:129]     # block 2: identical keys and values
+    v[0, :, 128:192] = v[0, :, 128:129]
+    kp, vp = o.build_pyramid(k, 4), o.build_pyramid(v, 4)
+    base = rng(24).integers(0, 4, size=(1, 2, 4, 8)).astype(np.int8)
+    outs = []
+    for l in range(4):
+        lev = base.copy()
+        lev[..., 2] = l
+        outs.append(o.pyramid_attention(q, kp, vp, lev, 128, 64, 0.35))
+    for l in range(1, 4):
+        np.testing.assert_allclose(outs[l][0], outs[0][0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(outs[l][1], outs[0][1], rtol=0, atol=1e-12)
+
+
+def test_unit_values_give_unit_output():
+    q, k, _ = small_case(25, N=300, d=4)
+    v = np.ones_like(k)
+    kp, vp = o.build_pyramid(k, 4), o.build_pyramid(v, 4)
+    lev = rng(26).integers(-1, 4, size=(1, 2, 3, 5)).astype(np.int8)
+    lev[..., 1] = 2
+    O, _ = o.pyramid_attention(q, kp, vp, lev, 128, 64, 0.5)
+    np.testing.assert_allclose(O, 1.0, rtol=0, atol=1e-13)
+
+
+def test_binary_mask_equals_masked_dense():
+    # L = 1: PSA reduces to binary block-sparse attention = dense attention with -inf on pruned blocks.
+    q, k, v = small_case(27, N=256, d=8)
+    kp, vp = o.build_pyramid(k, 1), o.build_pyramid(v, 1)
+    lev = rng(28).integers(-1, 1, size=(1, 2, 2, 4)).astype(np.int8)
+    lev[..., 1] = 0
+    O, L = o.pyramid_attention(q, kp, vp, lev, 128, 64, 0.35)
+    for h in range(2):
+        for i in range(2):
+            keep = np.repeat(lev[0, h, i] >= 0, 64)
+            for r in (i * 128, i * 128 + 77):
+                wl = [0.0 if kk else -math.inf for kk in keep]
+                idx = [t for t in range(256) if keep[t]]
+                ref_o, ref_l = brute_attention_row(q[0, h, r], k[0, h, idx], v[0, h, idx], [0.0] * len(idx), 0.35)
+                np.testing.assert_allclose(O[0, h, r], ref_o, rtol=0, atol=1e-12)
+                assert abs(L[0, h, r] - ref_l) < 1e-12
+
+
+def test_attention_key_shift_invariance():
+    q, k, v = small_case(29, N=512, d=8)
+    shift = rng(30).standard_normal(8)
+    lev = rng(31).integers(-1, 4, size=(1, 2, 4, 8)).astype(np.int8)
+    lev[..., 0] = 0
+    a = o.pyramid_attention(q, o.build_pyramid(k, 4), o.build_pyramid(v, 4), lev, 128, 64, 0.35)[0]
+    b = o.pyramid_attention(q, o.build_pyramid(k + shift, 4), o.build_pyramid(v, 4), lev, 128, 64, 0.35)[0]
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    q, k, v = small_case(32, H=4, Hkv=2, N=256, d=8)
+    lev = rng(33).integers(-1, 4, size=(1, 4, 2, 4)).astype(np.int8)
+    lev[..., 0] = 1
+    tau = (0.3, 0.5, 0.7, 0.9)
+    g = o.pyramid_attention(q, o.build_pyramid(k, 4), o.build_pyramid(v, 4), lev, 128, 64, 0.35)
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)   # heads [g0, g0, g1, g1]
+    m = o.pyramid_attention(q, o.build_pyramid(kr, 4), o.build_pyramid(vr, 4), lev, 128, 64, 0.35)
+    np.testing.assert_array_equal(g[0], m[0])
+    mg = o.estimate_mask(q, k, 128, 64, tau, 4, 0.35)
+    mm = o.estimate_mask(q, kr, 128, 64, tau, 4, 0.35)
+    np.testing.assert_array_equal(mg["levels"], mm["levels"])
+
+
+def test_all_pruned_row():
+    q, k, v = small_case(34, N=128, d=4)
+    lev = np.full((1, 2, 1, 2), -1, dtype=np.int8)
+    O, L = o.pyramid_attention(q, o.build_pyramid(k, 4), o.build_pyramid(v, 4), lev, 128, 64, 0.5)
+    assert np.all(O == 0) and np.all(np.isneginf(L))
+
+
+def test_effective_flops_closed_forms():
+    N, d = 2048, 64
+    for l in range(4):
+        lev = np.full((1, 2, 32, 32), l, dtype=np.int8)
+        assert o.effective_flops(lev, N, 64, 64, d) == 4.0 * 2 * N * N * d / 2 ** l
+    lev = np.full((1, 2, 32, 32), -1, dtype=np.int8)
+    assert o.effective_flops(lev, N, 64, 64, d) == 0.0
+
+
+# ----------------------------------------------------------------------------- hand-worked example
+
+def test_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    N, bk, bq, L, s = ex["N"], ex["kv_block"], ex["q_block"], ex["num_levels"], ex["scale"]
+    K = np.array(ex["K"], float).reshape(1, 1, N, 1)
+    V = np.array(ex["V"], float).reshape(1, 1, N, 1)
+    Q = np.array(ex["Q"], float).reshape(1, 1, N, 1)
+    kp, vp = o.build_pyramid(K, L), o.build_pyramid(V, L)
+    np.testing.assert_array_equal(kp[1][0, 0, :, 0], ex["level1_K"])
+    np.testing.assert_array_equal(vp[1][0, 0, :, 0], ex["level1_V"])
+    np.testing.assert_array_equal(o.pool_counts(N, 1), ex["level1_counts"])
+    p0, p1 = 1 / (1 + math.exp(-1)), 1 / (1 + math.exp(1))
+    for case in ex["cases"]:
+        m = o.estimate_mask(Q, K, bq, bk, case["thresholds"], L, s)
+        np.testing.assert_array_equal(m["kbar"][0, 0, :, 0], ex["kbar"])
+        np.testing.assert_array_equal(m["qbar"][0, 0, :, 0], ex["qbar"])
+        np.testing.assert_allclose(m["z"][0, 0, 0] - math.log(4), ex["z_minus_ln4"], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(m["p"][0, 0, 0], [p0, p1], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(m["cmass"][0, 0, 0], [0.0, p0], rtol=0, atol=1e-15)
+        np.testing.assert_array_equal(m["levels"][0, 0, 0], case["levels"])
+        w = [c * math.exp(a) for a, c in case["weights_exp_args"]]
+        o_ref = math.fsum(wi * vi for wi, vi in zip(w, case["values"])) / math.fsum(w)
+        lse_ref = math.log(math.fsum(w))
+        O, LSE = o.pyramid_attention(Q, kp, vp, m["levels"], bq, bk, s)
+        np.testing.assert_allclose(O[0, 0, :, 0], o_ref, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(LSE[0, 0], lse_ref, rtol=0, atol=1e-13)
