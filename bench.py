@@ -1,0 +1,197 @@
+"""Benchmark of the MI355X Pyramid Sparse Attention forward path (one GPU).
+
+    python bench.py [--steps K] [--warmup W] [--workload wan13b] [--no-cpu-baseline]
+
+A step is one pass of the whole forward path over one batch of resident inputs:
+psa_build_pyramid, psa_estimate_mask and psa_attention_fwd, enqueued on one stream.
+W untimed steps, then K timed steps bracketed by device synchronisation; HIP events
+around every call give per-call times (the attention call is a single kernel launch,
+the roofline's kernel).
+
+Throughput is effective TFLOP/s: FLOPs of QK^T and PV on the retained pooled rows
+only (sum over retained blocks of 4 * rows * pooled_rows * d), divided by the step
+time. The CPU baseline times the float64 oracle on four heads of the same workload.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan13b_traffic.txt")
+ATTN_SOURCE = os.path.join(ROOT, "level_pooled_kv_amd", "csrc", "psa_attention.hip")
+
+
+def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, d: int) -> float:
+    """sum over retained (b,h,i,j): 4 * m_i * ceil(n_j / 2^l) * d."""
+    nqb, nkb = level_map.shape[-2], level_map.shape[-1]
+    m = np.minimum(q_block, N - np.arange(nqb) * q_block).astype(np.float64)
+    n = np.minimum(kv_block, N - np.arange(nkb) * kv_block)
+    lm = level_map.reshape(-1, nqb, nkb)
+    total = 0.0
+    for l in range(4):
+        rows = (-(-n // (1 << l))).astype(np.float64)
+        sel = (lm == l).astype(np.float64)
+        total += float(np.einsum("xij,i,j->", sel, m, rows))
+    return 4.0 * d * total
+
+
+def level_histogram(level_map: np.ndarray):
+    return {str(l): int((level_map == l).sum()) for l in (-1, 0, 1, 2, 3)}
+
+
+def traffic_from_profile():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
+    was taken on the current attention source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if kv.get("attention_source_sha256") != src:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, tau):
+    """Oracle (float64 NumPy) on a bounded sample: every step for query heads 0..3 (and their KV heads)."""
+    from threadpoolctl import threadpool_info
+    from oracle import psa_oracle as o
+
+    t0 = time.perf_counter()
+    nh = min(4, w.H)
+    qh = q[:, :nh].astype(np.float64)
+    kh = k[:, :nh].astype(np.float64)
+    vh = v[:, :nh].astype(np.float64)
+    res = o.run_forward(qh, kh, vh, w.q_block, w.kv_block, tau, w.num_levels, w.scale, w.dtype,
+                        w.n_dense_prefix)
+    dt = time.perf_counter() - t0
+    fl = o.effective_flops(res["mask"]["levels"], w.N, w.q_block, w.kv_block, w.d)
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: all three steps (pyramid, mask, attention) for heads 0..{nh - 1} of {w.H}, "
+                      f"{fl:.3e} effective FLOPs in {dt:.1f} s, float64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the forward path has no cross-GPU step here; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import level_pooled_kv_amd as psa
+    from synth import get as get_workload, generate
+
+    w = get_workload(args.workload)
+    tau = w.thresholds()
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = generate(w, "q"), generate(w, "k"), generate(w, "v")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    qd = torch.from_numpy(q).to(dt).to(dev)
+    kd = torch.from_numpy(k).to(dt).to(dev)
+    vd = torch.from_numpy(v).to(dt).to(dev)
+    prob = psa.Problem(B=w.B, H=w.H, H_kv=w.H_kv, N=w.N, d=w.d, q_block=w.q_block, kv_block=w.kv_block,
+                       num_levels=w.num_levels, dtype=w.dtype)
+    R = prob.pyramid_rows
+    k_pyr = torch.empty((w.B, w.H_kv, R, w.d), dtype=dt, device=dev)
+    v_pyr = torch.empty_like(k_pyr)
+    k_bar = torch.empty((w.B, w.H_kv, prob.nkb, w.d), dtype=torch.float32, device=dev)
+    level_map = torch.empty((w.B, w.H, prob.nqb, prob.nkb), dtype=torch.int8, device=dev)
+    ws = torch.empty(prob.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(qd)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        psa.psa_build_pyramid(prob, kd, vd, k_pyr, v_pyr, k_bar)
+        if ev: ev[1].record()
+        psa.psa_estimate_mask(prob, qd, k_bar, tau, w.n_dense_prefix, level_map=level_map, workspace=ws)
+        if ev: ev[2].record()
+        psa.psa_attention_fwd(prob, qd, kd, vd, k_pyr, v_pyr, level_map, o=o)
+        if ev: ev[3].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])   # ms
+    pyr_ms, mask_ms, attn_ms = (float(np.mean(per[:, i])) for i in range(3))
+
+    lm = level_map.cpu().numpy()
+    flops = effective_flops(lm, w.N, w.q_block, w.kv_block, w.d)
+    rho = flops / w.dense_flops()
+    esz = 2 if w.dtype == "bf16" else 4
+    kv_bytes = 2 * w.B * w.H_kv * w.N * w.d * esz
+    pyr_bytes = kv_bytes + 2 * w.B * w.H_kv * R * w.d * esz + k_bar.numel() * 4
+    mask_bytes = w.B * w.H * w.N * w.d * esz + k_bar.numel() * 4 + lm.size
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile()
+
+    result = {
+        "metric": "PSA fwd ms/call + effective TFLOP/s (% MFMA peak) at 32760 tok, ~91% sparsity",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "B": w.B, "H": w.H, "H_kv": w.H_kv,
+                   "N": w.N, "d": w.d, "q_block": w.q_block, "kv_block": w.kv_block,
+                   "num_levels": w.num_levels, "thresholds": list(tau), "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "pyramid_attn_fwd_kernel<bf16,128,4>"},
+        "calls_ms": {"build_pyramid": round(pyr_ms, 4), "estimate_mask": round(mask_ms, 4),
+                     "attention_fwd": round(attn_ms, 4)},
+        "effective_flops": flops, "flop_fraction_rho": round(rho, 5),
+        "hbm": {"build_pyramid_GBps": round(pyr_bytes / (pyr_ms * 1e-3) / 1e9, 1),
+                "build_pyramid_frac": round(pyr_bytes / (pyr_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "estimate_mask_GBps": round(mask_bytes / (mask_ms * 1e-3) / 1e9, 1),
+                "estimate_mask_frac": round(mask_bytes / (mask_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "build_pyramid_bytes": pyr_bytes, "estimate_mask_bytes": mask_bytes},
+        "levels": level_histogram(lm),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on one head", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, tau)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * psa.h — C ABI of the MI355X (gfx950) Pyramid Sparse Attention forward path.
+ *
+ * Pyramid Sparse Attention (PSA; "PSA: Pyramid Sparse Attention for Efficient
+ * Video Understanding and Generation", abstract) replaces binary keep/drop block
+ * masks with a multi-level pooled KV pyramid: every (query block, KV block) pair
+ * gets a pool level, fine for important blocks, coarse for less important ones,
+ * or is pruned. The forward pass has three steps, one entry point each:
+ *
+ *   psa_build_pyramid  — average-pooled K/V levels 1..L-1 and per-block mean keys
+ *   psa_estimate_mask  — block importance and the threshold-based level map
+ *   psa_attention_fwd  — attention over mixed-resolution keys, one softmax
+ *
+ * Tensors (all row-major, contiguous, head_dim innermost):
+ *   q      [B, H,    N, d]          I/O dtype
+ *   k, v   [B, H_kv, N, d]          I/O dtype; query head h reads KV head h / (H / H_kv)
+ *   k_pyr, v_pyr [B, H_kv, R, d]    I/O dtype, R = psa_pyramid_rows(): level 1, then
+ *                                   level 2, ... concatenated along the row axis;
+ *                                   level l has ceil(N / 2^l) rows
+ *   k_bar  [B, H_kv, nkb, d]        float32 mean key of each 64-token KV block
+ *   level_map [B, H, nqb, nkb]      int8: level 0..L-1, or -1 = pruned
+ *   o      [B, H, N, d]             I/O dtype;  lse [B, H, N] float32 (natural log)
+ * with nqb = ceil(N / q_block), nkb = ceil(N / kv_block).
+ *
+ * Conventions shared by every entry point:
+ *  - Device pointers point to memory of the current HIP device; the caller owns
+ *    every buffer, keeps it alive until the work on `stream` has finished, and the
+ *    library keeps no pointer after a call returns. Device pointers must be
+ *    16-byte aligned. `thresholds` is a host pointer.
+ *  - Calls only enqueue kernels on `stream` and return without synchronising.
+ *    The library holds no state and allocates no memory; calls are thread-safe.
+ *  - Arguments are checked before anything is launched: invalid values return
+ *    PSA_ERR_INVALID_ARGUMENT, valid shapes outside the supported envelope
+ *    PSA_ERR_UNSUPPORTED, a short workspace PSA_ERR_WORKSPACE_TOO_SMALL; a failed
+ *    launch returns PSA_ERR_HIP. No call aborts, throws or prints;
+ *    psa_last_error() gives the calling thread's detail message.
+ *  - Arithmetic: pooling, block means and block scores accumulate in float32;
+ *    attention multiplies bf16 operands on the matrix cores with float32
+ *    accumulation and a float32 online softmax. float32 I/O is rounded to bf16
+ *    on its way into the matrix cores.
+ */
+#ifndef PSA_H_
+#define PSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PSA_OK = 0,
+  PSA_ERR_INVALID_ARGUMENT = 1,
+  PSA_ERR_UNSUPPORTED = 2,
+  PSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PSA_ERR_HIP = 4
+} psa_status_t;
+
+typedef enum { PSA_F32 = 0, PSA_BF16 = 1 } psa_dtype_t;
+
+/* Which call a workspace size is asked for. */
+typedef enum { PSA_WS_ESTIMATE_MASK = 0, PSA_WS_ATTENTION_FWD = 1 } psa_workspace_kind_t;
+
+typedef struct {
+  int32_t B, H, H_kv, N, d;   /* d in {64, 128}; H % H_kv == 0                        */
+  int32_t q_block;            /* query block size: 64 or 128                           */
+  int32_t kv_block;           /* KV block size: 64                                     */
+  int32_t num_levels;         /* L in [1, 4]: level l pools 2^l tokens                 */
+  psa_dtype_t dtype;          /* I/O dtype of q, k, v, k_pyr, v_pyr, o                 */
+  float scale;                /* softmax scale; <= 0 selects 1/sqrt(d)                 */
+} psa_problem_t;
+
+/* Rows of the concatenated pyramid: sum over l = 1..L-1 of ceil(N / 2^l).
+ * Returns 0 for a NULL or malformed problem. */
+size_t psa_pyramid_rows(const psa_problem_t* prob);
+
+/* Device workspace, in bytes, that `kind`'s call needs (0 if none; also 0 for a
+ * NULL or malformed problem). */
+size_t psa_workspace_bytes(const psa_problem_t* prob, psa_workspace_kind_t kind);
+
+/* Checks a problem description alone (no pointers): PSA_OK, INVALID_ARGUMENT or
+ * UNSUPPORTED, with the reason in psa_last_error(). */
+psa_status_t psa_check_problem(const psa_problem_t* prob);
+
+/*
+ * Step 1, the pyramid ("pyramid KV block construction by progressive pooling":
+ * top168.com article, paragraph naming the three components; pool factor 2^level
+ * and average pooling over tokens: skillmd.com page, "Pooled KV cache creation").
+ * For l = 1..L-1, pooled row p of level l is the mean of K (and of V) over tokens
+ * [p*2^l, min((p+1)*2^l, N)); a ragged last group is averaged over the tokens it
+ * has. Results are rounded to the I/O dtype (ties to even). k_bar[j] is the
+ * float32 mean of K over KV block j (its n_j = min(64, N - 64 j) tokens).
+ * k_pyr and v_pyr may be NULL when num_levels == 1.
+ */
+psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const void* v,
+                               void* k_pyr, void* v_pyr, float* k_bar, hipStream_t stream);
+
+/*
+ * Step 2, the multi-level mask ("a multi-level mask generator that assigns a
+ * level by the importance of each query-block / KV-block pair": top168.com,
+ * three-components paragraph; threshold-based assignment: same page, ablation
+ * paragraph; scoring a block by the query against the block's mean key:
+ * skillmd.com, "Block importance scoring").
+ * For query block i of head h (mean query qbar_i over its rows) and KV block j:
+ *   z_ij = scale * <qbar_i, k_bar_j> + ln n_j,   p_ij = softmax over j of z_ij.
+ * Blocks are ranked by z descending, ties by j ascending; C_ij is the total p of
+ * the blocks ranked strictly ahead of j. level_ij = min{l : C_ij < thresholds[l]},
+ * or -1 (pruned) if there is none. Finally every KV block that overlaps tokens
+ * [0, n_dense_prefix) is set to level 0 for every query block.
+ * thresholds: host array of num_levels floats, nondecreasing, each in [0, 1].
+ * cmass_out (nullable): C as float32 [B, H, nqb, nkb].
+ * workspace: psa_workspace_bytes(prob, PSA_WS_ESTIMATE_MASK) bytes of device memory.
+ * Supported: nkb <= 2048 (N <= 131072).
+ */
+psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const float* k_bar,
+                               const float* thresholds, int32_t n_dense_prefix,
+                               int8_t* level_map, float* cmass_out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Step 3, attention over mixed-resolution keys with one softmax ("adaptive
+ * pyramid attention that keeps the probability distribution consistent":
+ * top168.com, three-components paragraph; decoupled logical-block / hardware-tile
+ * execution: chatpaper.ai abstract and top168.com kernel paragraph).
+ * Query row r of block i attends to every pooled row p of every retained KV block
+ * j (level l = level_map[.., i, j] >= 0; block j owns rows
+ * [j*64/2^l, ceil((j*64 + n_j)/2^l)) of level l, level 0 being K/V themselves), with
+ * logit a_rp = scale * <q_r, K^l_p> + ln c_p, c_p the number of tokens row p
+ * averages. O_r = sum_p e^{a_rp} V^l_p / sum_p e^{a_rp}; lse_r = ln sum_p e^{a_rp}.
+ * A row whose query block retains nothing gets O = 0 and lse = -inf.
+ * lse may be NULL. workspace may be NULL when psa_workspace_bytes(prob,
+ * PSA_WS_ATTENTION_FWD) is 0. k_pyr, v_pyr may be NULL when num_levels == 1.
+ * level_map values outside [-1, L-1] are treated as -1 (pruned).
+ */
+psa_status_t psa_attention_fwd(const psa_problem_t* prob, const void* q, const void* k,
+                               const void* v, const void* k_pyr, const void* v_pyr,
+                               const int8_t* level_map, void* o, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code ("PSA_OK", ...); never NULL. */
+const char* psa_status_string(psa_status_t status);
+
+/* Detail of the calling thread's last non-OK return ("" if none); valid until the
+ * thread's next psa_* call. */
+const char* psa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSA_H_ */

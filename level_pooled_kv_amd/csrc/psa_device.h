@@ -1,0 +1,69 @@
+// Device-side helpers shared by the gfx950 kernels of the PSA forward path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16_t { uint16_t bits; };   // storage type of bf16 tensors
+
+// 16 bytes moved as one unit.
+struct alignas(16) U128 { uint32_t w[4]; };
+
+__device__ __forceinline__ U128 ld128(const void* p) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  U128 r; r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w; return r;
+}
+__device__ __forceinline__ void st128(void* p, const U128& r) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v; v[0] = (__bf16)lo; v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Element traits of an I/O dtype: how many elements one 16-byte load holds.
+template <typename T> struct io_traits;
+template <> struct io_traits<bf16_t> { static constexpr int per16 = 8; };
+template <> struct io_traits<float>  { static constexpr int per16 = 4; };
+
+// Unpack one 16-byte chunk into floats.
+template <typename T> __device__ __forceinline__ void unpack16(const U128& r, float* out);
+template <> __device__ __forceinline__ void unpack16<bf16_t>(const U128& r, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { out[2 * i] = bf16_lo(r.w[i]); out[2 * i + 1] = bf16_hi(r.w[i]); }
+}
+template <> __device__ __forceinline__ void unpack16<float>(const U128& r, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(r.w[i]);
+}
+
+// Pack floats of one 16-byte chunk into the I/O dtype (round to nearest even).
+template <typename T> __device__ __forceinline__ U128 pack16(const float* in);
+template <> __device__ __forceinline__ U128 pack16<bf16_t>(const float* in) {
+  U128 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.w[i] = pack_bf16x2(in[2 * i], in[2 * i + 1]);
+  return r;
+}
+template <> __device__ __forceinline__ U128 pack16<float>(const float* in) {
+  U128 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.w[i] = __float_as_uint(in[i]);
+  return r;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace psa

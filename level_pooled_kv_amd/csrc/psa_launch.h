@@ -1,0 +1,45 @@
+// Host-side launch descriptions passed from the C ABI layer to each step's launcher.
+// Every field has already been validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psa {
+
+constexpr int kKvBlock = 64;       // tokens per KV block
+constexpr int kMaxLevels = 4;      // levels 0..3: pool factors 1, 2, 4, 8
+constexpr int kMaxKvBlocks = 2048; // per sequence (LDS capacity of the mask sort and the attention block lists)
+
+struct PyramidArgs {
+  const void* k; const void* v; void* k_pyr; void* v_pyr; float* k_bar;
+  int B, H_kv, N, d, nkb, L;
+  bool bf16;
+  int64_t pyr_rows;              // rows of the concatenated pyramid
+  int off[kMaxLevels];           // row offset of level l (l >= 1) in the pyramid
+};
+
+struct MaskArgs {
+  const void* q; const float* k_bar; int8_t* level_map; float* cmass; float* qbar;
+  int B, H, H_kv, N, d, q_block, nqb, nkb, L, n_dense_prefix;
+  bool bf16;
+  float scale;
+  float tau[kMaxLevels];
+};
+
+struct AttnArgs {
+  const void* q; const void* k; const void* v; const void* k_pyr; const void* v_pyr;
+  const int8_t* level_map; void* o; float* lse;
+  int B, H, H_kv, N, d, q_block, nqb, nkb, L;
+  bool bf16;
+  float scale;
+  int64_t pyr_rows;
+  int off[kMaxLevels];           // row offset of level l (l >= 1) in the pyramid
+  int rows[kMaxLevels];          // ceil(N / 2^l)
+};
+
+hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t stream);
+hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace psa

@@ -1,0 +1,132 @@
+"""Host-only checks of the C ABI: the library loads, exports every function include/psa.h
+declares, derives sizes correctly and rejects invalid arguments before launching anything
+(these calls never reach the GPU, so they run without one)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psa.h")
+
+
+@pytest.fixture(scope="module")
+def psa():
+    import level_pooled_kv_amd as lib
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(psa):
+    names = declared_functions()
+    assert len(names) >= 8
+    assert set(names) == set(psa.EXPORTED)
+    for n in names:
+        assert hasattr(psa.lib, n), n
+
+
+def prob(psa, **kw):
+    base = dict(B=1, H=12, H_kv=12, N=32760, d=128, q_block=128, kv_block=64, num_levels=4, dtype="bf16")
+    base.update(kw)
+    return psa.Problem(**base)
+
+
+def test_sizes(psa):
+    p = prob(psa)
+    assert p.pyramid_rows == sum(math.ceil(32760 / 2 ** l) for l in (1, 2, 3))
+    assert p.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK) == 1 * 12 * 256 * 128 * 4
+    assert p.workspace_bytes(psa.PSA_WS_ATTENTION_FWD) == 0
+    assert prob(psa, num_levels=1).pyramid_rows == 0
+    assert prob(psa, N=2045, num_levels=2).pyramid_rows == 1023
+    assert prob(psa, d=96).pyramid_rows == 0          # malformed -> 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(N=-5), 1), (dict(H=12, H_kv=5), 1), (dict(num_levels=0), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(d=96), 2), (dict(q_block=32), 2), (dict(kv_block=128), 2), (dict(num_levels=5), 2),
+    (dict(N=64 * 2048 + 1), 2),
+])
+def test_check_problem_rejects(psa, kw, status):
+    p = prob(psa, **kw)
+    st = psa.lib.psa_check_problem(ctypes.byref(p.c()))
+    assert st == status, (kw, st, psa.last_error())
+    assert psa.last_error() != ""
+
+
+def test_check_problem_accepts_workloads(psa):
+    from synth import WORKLOADS
+    for w in WORKLOADS.values():
+        p = psa.Problem(B=w.B, H=w.H, H_kv=w.H_kv, N=w.N, d=w.d, q_block=w.q_block, num_levels=w.num_levels,
+                        dtype=w.dtype)
+        assert psa.lib.psa_check_problem(ctypes.byref(p.c())) == 0, (w.name, psa.last_error())
+
+
+FAKE = ctypes.c_void_p(4096)       # aligned, never dereferenced: every call below fails validation first
+MISALIGNED = ctypes.c_void_p(4104)
+
+
+def test_build_pyramid_rejects_bad_pointers(psa):
+    p = prob(psa).c()
+    f = psa.lib.psa_build_pyramid
+    assert f(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert "k is NULL" in psa.last_error()
+    assert f(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None) == 1
+    assert f(ctypes.byref(p), FAKE, MISALIGNED, FAKE, FAKE, FAKE, None) == 1
+    assert "aligned" in psa.last_error()
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    bad = prob(psa, d=80).c()
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+
+
+def tau(*vals):
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+def test_estimate_mask_rejects(psa):
+    p = prob(psa)
+    c = p.c()
+    ws = p.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
+    f = psa.lib.psa_estimate_mask
+    ok_tau = tau(0.1, 0.2, 0.3, 0.4)
+    # thresholds: NaN, out of range, decreasing, NULL
+    for t in (tau(0.1, float("nan"), 0.3, 0.4), tau(-0.1, 0.2, 0.3, 0.4), tau(0.1, 0.2, 1.5, 1.6),
+              tau(0.3, 0.2, 0.4, 0.5)):
+        assert f(ctypes.byref(c), FAKE, FAKE, t, 0, FAKE, None, FAKE, ws, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, None, 0, FAKE, None, FAKE, ws, None) == 1
+    # n_dense_prefix outside [0, N]
+    assert f(ctypes.byref(c), FAKE, FAKE, ok_tau, -1, FAKE, None, FAKE, ws, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, ok_tau, p.N + 1, FAKE, None, FAKE, ws, None) == 1
+    # workspace too small
+    assert f(ctypes.byref(c), FAKE, FAKE, ok_tau, 0, FAKE, None, FAKE, ws - 1, None) == 3
+    assert "needed" in psa.last_error()
+    # NULL / misaligned outputs
+    assert f(ctypes.byref(c), FAKE, FAKE, ok_tau, 0, None, None, FAKE, ws, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, ok_tau, 0, FAKE, MISALIGNED, FAKE, ws, None) == 1
+
+
+def test_attention_rejects(psa):
+    c = prob(psa).c()
+    f = psa.lib.psa_attention_fwd
+    assert f(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, None, 0, None) == 1
+    c1 = prob(psa, num_levels=1, d=64).c()     # pyramid pointers may be NULL at one level: passes
+    # validation, so only check the unsupported path here (no launch without a GPU)
+    bad = prob(psa, q_block=256).c()
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, None, 0, None) == 2
+    del c1
+
+
+def test_status_strings(psa):
+    names = [psa.status_string(s) for s in range(5)]
+    assert names == ["PSA_OK", "PSA_ERR_INVALID_ARGUMENT", "PSA_ERR_UNSUPPORTED",
+                     "PSA_ERR_WORKSPACE_TOO_SMALL", "PSA_ERR_HIP"]
+    assert psa.status_string(99) == "PSA_ERR_UNKNOWN"

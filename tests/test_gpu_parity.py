@@ -1,0 +1,249 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
+
+Every case prints its name before touching the GPU. Small cases compare every
+output element; the full-size workloads compare the pyramid, k_bar and the level
+map in full and the attention output on sampled query blocks (the oracle
+computes those one by one), in the same launch configuration the benchmark uses.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import psa_oracle as o
+from synth import get as get_workload, generate, random_qkv
+from tests.psa_check import (check_attention, check_cmass, check_kbar, check_mask, check_pyramid,
+                              lse_tolerance, to_device, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def psa():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import level_pooled_kv_amd as lib
+    return lib
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def gpu_levels_list(t: torch.Tensor, N: int, L: int):
+    """Split a [B,H_kv,R,d] device pyramid into host arrays per level 1..L-1."""
+    out, off = [], 0
+    for l in range(1, L):
+        R = -(-N // 2 ** l)
+        out.append(to_host(t[:, :, off:off + R]))
+        off += R
+    return out
+
+
+def run_small(psa, label, q, k, v, *, H, H_kv, d, q_block, L, dtype, tau, n_dense_prefix=0, scale=None):
+    B, _, N, _ = q.shape
+    s = 1.0 / math.sqrt(d) if scale is None else scale
+    prob = psa.Problem(B=B, H=H, H_kv=H_kv, N=N, d=d, q_block=q_block, kv_block=64, num_levels=L,
+                       dtype=dtype, scale=0.0 if scale is None else scale)
+    say(f"{label}: B={B} H={H} H_kv={H_kv} N={N} d={d} q_block={q_block} L={L} {dtype} tau={tau}")
+    ora = o.run_forward(q, k, v, q_block, 64, tau, L, s, dtype, n_dense_prefix)
+    qd, kd, vd = to_device(q, dtype), to_device(k, dtype), to_device(v, dtype)
+
+    # step 1
+    kp, vp, kbar = psa.psa_build_pyramid(prob, kd, vd)
+    torch.cuda.synchronize()
+    if L > 1:
+        check_pyramid(gpu_levels_list(kp, N, L), ora["kpyr"][1:], dtype, label + " k_pyr", np.abs(k).max())
+        check_pyramid(gpu_levels_list(vp, N, L), ora["vpyr"][1:], dtype, label + " v_pyr", np.abs(v).max())
+    check_kbar(to_host(kbar), ora["mask"]["kbar"], label)
+
+    # step 2
+    lev, cm = psa.psa_estimate_mask(prob, qd, kbar, tau, n_dense_prefix, want_cmass=True)
+    torch.cuda.synchronize()
+    lev_gpu = lev.cpu().numpy()
+    nacc = check_mask(lev_gpu, ora["mask"], tau, L, n_dense_prefix, label=label)
+    check_cmass(to_host(cm), ora["mask"], label)
+
+    # step 3 on the oracle's level map
+    lev_ora = torch.from_numpy(ora["mask"]["levels"]).cuda()
+    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lev_ora, want_lse=True)
+    torch.cuda.synchronize()
+    mx, mean = check_attention(to_host(out), ora["O"], label)
+    lse_g, lse_r = to_host(lse), ora["LSE"]
+    fin = np.isfinite(lse_r)
+    assert np.array_equal(np.isfinite(lse_g), fin), label
+    if fin.any():
+        tol = lse_tolerance(q, k, s, dtype)
+        assert np.all(np.abs(lse_g - lse_r)[fin] <= tol[fin]), (label, np.abs(lse_g[fin] - lse_r[fin]).max())
+
+    # end to end: the GPU's own mask given to both sides
+    if nacc:
+        out2, _ = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lev)
+        torch.cuda.synchronize()
+        O2, _ = o.pyramid_attention(q, ora["kpyr"], ora["vpyr"], lev_gpu, q_block, 64, s)
+        check_attention(to_host(out2), O2, label + " e2e")
+    say(f"{label}: ok (mask mismatches accepted: {nacc}, O max {mx:.2e} mean {mean:.2e})")
+    return ora, lev_gpu
+
+
+# ------------------------------------------------------------------------------ small cases
+
+def test_tiny_workload_full(psa):
+    w = get_workload("tiny")
+    q, k, v = generate(w, "q"), generate(w, "k"), generate(w, "v")
+    run_small(psa, "tiny workload", q, k, v, H=w.H, H_kv=w.H_kv, d=w.d, q_block=w.q_block,
+              L=w.num_levels, dtype=w.dtype, tau=w.thresholds())
+
+
+RAGGED = [
+    # label, N, d, q_block, L, dtype, H, H_kv
+    ("ragged N=2045 d128 bq128 gqa", 2045, 128, 128, 4, "bf16", 4, 2),
+    ("ragged N=130 d64 bq64", 130, 64, 64, 4, "bf16", 2, 2),
+    ("N=64 single block d128 bq64", 64, 128, 64, 4, "bf16", 1, 1),
+    ("N=1 d64 bq128", 1, 64, 128, 4, "bf16", 1, 1),
+    ("N=1000 d128 bq64 L=2", 1000, 128, 64, 2, "bf16", 2, 1),
+    ("N=777 d64 bq128 L=3 f32", 777, 64, 128, 3, "f32", 2, 2),
+    ("N=1536 d128 bq128 L=1", 1536, 128, 128, 1, "bf16", 2, 2),
+    ("N=900 d128 bq128 f32", 900, 128, 128, 4, "f32", 2, 1),
+    ("N=4100 d64 bq128 bf16", 4100, 64, 128, 4, "bf16", 3, 3),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+def test_ragged_shapes(psa, case):
+    label, N, d, bq, L, dtype, H, H_kv = case
+    q, k, v = random_qkv(N + d + L, 1, H, H_kv, N, d, dtype)
+    tau = (0.3, 0.55, 0.75, 0.9)[:L]
+    run_small(psa, label, q, k, v, H=H, H_kv=H_kv, d=d, q_block=bq, L=L, dtype=dtype, tau=tau)
+
+
+def test_dense_prefix_and_custom_scale(psa):
+    q, k, v = random_qkv(77, 1, 2, 2, 1200, 64, "bf16")
+    run_small(psa, "dense prefix 226 + scale 0.2", q, k, v, H=2, H_kv=2, d=64, q_block=128, L=4,
+              dtype="bf16", tau=(0.05, 0.2, 0.4, 0.6), n_dense_prefix=226, scale=0.2)
+
+
+def test_all_level0_equals_dense(psa):
+    q, k, v = random_qkv(5, 1, 2, 2, 1000, 128, "bf16")
+    ora, lev = run_small(psa, "thresholds 1 -> dense", q, k, v, H=2, H_kv=2, d=128, q_block=128, L=4,
+                         dtype="bf16", tau=(1.0, 1.0, 1.0, 1.0))
+    assert np.all(lev == 0)
+    Od, _ = o.dense_attention(q, k, v, 1 / math.sqrt(128))
+    check_attention(ora["O"], Od, "oracle vs dense")
+
+
+def test_all_pruned(psa):
+    q, k, v = random_qkv(6, 1, 2, 2, 700, 64, "bf16")
+    prob = psa.Problem(B=1, H=2, H_kv=2, N=700, d=64, q_block=128, num_levels=4, dtype="bf16")
+    say("all pruned")
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    kp, vp, kbar = psa.psa_build_pyramid(prob, kd, vd)
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, (0.0, 0.0, 0.0, 0.0))
+    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lev, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(lev == -1)
+    assert torch.all(out == 0)
+    assert torch.all(torch.isneginf(lse))
+
+
+def test_identical_key_block_level_invariant(psa):
+    # a KV block of identical keys and values gives the same output at every level
+    q, k, v = random_qkv(8, 1, 1, 1, 512, 128, "bf16")
+    k[0, 0, 128:192] = k[0, 0, 128:129]
+    v[0, 0, 128:192] = v[0, 0, 128:129]
+    prob = psa.Problem(B=1, H=1, H_kv=1, N=512, d=128, q_block=128, num_levels=4, dtype="bf16")
+    say("identical-key block at levels 0..3")
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    kp, vp, _ = psa.psa_build_pyramid(prob, kd, vd)
+    base = np.random.default_rng(3).integers(0, 4, size=(1, 1, 4, 8)).astype(np.int8)
+    outs = []
+    for l in range(4):
+        lev = base.copy()
+        lev[..., 2] = l
+        out, _ = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, torch.from_numpy(lev).cuda())
+        outs.append(to_host(out))
+    torch.cuda.synchronize()
+    for l in range(1, 4):
+        assert np.abs(outs[l] - outs[0]).max() < 2e-2
+
+
+def test_deterministic(psa):
+    q, k, v = random_qkv(9, 1, 2, 2, 3000, 128, "bf16")
+    prob = psa.Problem(B=1, H=2, H_kv=2, N=3000, d=128, q_block=128, num_levels=4, dtype="bf16")
+    say("determinism")
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    r1 = psa.psa_forward(prob, qd, kd, vd, (0.2, 0.4, 0.6, 0.8))
+    r2 = psa.psa_forward(prob, qd, kd, vd, (0.2, 0.4, 0.6, 0.8))
+    torch.cuda.synchronize()
+    for key in r1:
+        assert torch.equal(r1[key], r2[key]), key
+
+
+# ------------------------------------------------------------------------------ full-size workloads
+
+def full_workload(psa, name, n_items=8, seed=0):
+    w = get_workload(name)
+    tau = w.thresholds()
+    L = w.num_levels
+    s = w.scale
+    say(f"{name}: generating inputs B={w.B} H={w.H} H_kv={w.H_kv} N={w.N} d={w.d}")
+    q, k, v = generate(w, "q"), generate(w, "k"), generate(w, "v")
+    prob = psa.Problem(B=w.B, H=w.H, H_kv=w.H_kv, N=w.N, d=w.d, q_block=w.q_block, kv_block=w.kv_block,
+                       num_levels=L, dtype=w.dtype)
+    qd, kd, vd = to_device(q, w.dtype), to_device(k, w.dtype), to_device(v, w.dtype)
+    say(f"{name}: GPU pyramid + mask")
+    kp, vp, kbar = psa.psa_build_pyramid(prob, kd, vd)
+    lev, cm = psa.psa_estimate_mask(prob, qd, kbar, tau, w.n_dense_prefix, want_cmass=True)
+    torch.cuda.synchronize()
+
+    say(f"{name}: oracle pyramid per KV head")
+    kbar_g = to_host(kbar)
+    kbar_o = np.empty_like(kbar_g)
+    kp_levels = {}
+    for g in range(w.H_kv):
+        for name_t, x, dev in (("k", k, kp), ("v", v, vp)):
+            lv = o.build_pyramid(x[:, g:g + 1], L)
+            lv_io = [x[:, g:g + 1].astype(np.float64)] + [o.round_to_io(a, w.dtype) for a in lv[1:]]
+            check_pyramid(gpu_levels_list(dev[:, g:g + 1], w.N, L), lv_io[1:], w.dtype, f"{name} {name_t} g={g}",
+                          np.abs(x[:, g]).max())
+            kp_levels[(name_t, g)] = lv_io
+        kbar_o[:, g] = o.block_means(k[:, g], w.kv_block)
+    check_kbar(kbar_g, kbar_o, name)
+
+    say(f"{name}: oracle mask")
+    qbar = np.concatenate([o.block_means(q[:, h:h + 1], w.q_block) for h in range(w.H)], axis=1)
+    z = o.block_scores(qbar, kbar_o, o.block_sizes(w.N, w.kv_block), s)
+    p = o.softmax_rows(z)
+    C = o.cumulative_mass(z, p)
+    lev_o = o.assign_levels(C, tau, L, w.n_dense_prefix, w.kv_block)
+    lev_g = lev.cpu().numpy()
+    nacc = check_mask(lev_g, {"z": z, "p": p, "cmass": C, "levels": lev_o}, tau, L, w.n_dense_prefix,
+                      label=name)
+
+    say(f"{name}: GPU attention on the oracle's level map")
+    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, torch.from_numpy(lev_o).cuda(), want_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    items = {(0, w.H - 1, w.nqb - 1), (0, 0, 0)}
+    while len(items) < n_items:
+        items.add((int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.nqb))))
+    worst = 0.0
+    for (b, h, i) in sorted(items):
+        g = o.kv_head_of(h, w.H, w.H_kv)
+        keys, vals, logc = o.gather_keys(lev_o[b, h, i], w.N, w.kv_block,
+                                         [a[b, 0] for a in kp_levels[("k", g)]],
+                                         [a[b, 0] for a in kp_levels[("v", g)]])
+        r0, r1 = i * w.q_block, min((i + 1) * w.q_block, w.N)
+        O_ref, lse_ref = o.attention_rows(q[b, h, r0:r1].astype(np.float64), keys, vals, logc, s)
+        og = to_host(out[b, h, r0:r1])
+        mx, _ = check_attention(og, O_ref, f"{name} item {(b, h, i)}", rows=np.ones(r1 - r0, bool))
+        worst = max(worst, mx)
+        lg = to_host(lse[b, h, r0:r1])
+        tol = lse_tolerance(q[b:b + 1, h:h + 1, r0:r1], k[b:b + 1, g:g + 1], s, w.dtype)[0, 0]
+        assert np.all(np.abs(lg - lse_ref) <= tol), (name, (b, h, i), np.abs(lg - lse_ref).max())
+    say(f"{name}: ok (mask mismatches accepted: {nacc} of {lev_o.size}; O max err {worst:.2e})")
+
+
+@pytest.mark.parametrize("name", ["wan13b", "cogvx5b", "qwen7b", "wan14b"])
+def test_full_workload(psa, name):
+    full_workload(psa, name)
