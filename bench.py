@@ -98,7 +98,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan13b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "copies": 3}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the forward path has no cross-GPU step here; "
               "run with --gpus 1", file=sys.stderr)

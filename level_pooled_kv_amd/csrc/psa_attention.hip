@@ -20,16 +20,18 @@
 //    same ln(2^l) bias, so the bias folds into the running max at no per-logit
 //    cost; only the last tile of a level (padding, ragged tail) takes a per-key
 //    correction path.
-//  * Tiles are staged global -> registers -> LDS with one tile of prefetch (double
-//    buffered LDS). K is stored row-major with an XOR swizzle of its 16-byte
-//    chunks; V is stored transposed (V^T, key-contiguous) so it can feed the
-//    matrix core as the A operand of O^T = V^T P^T.
+//  * Tiles are double buffered in LDS with one tile of prefetch. bf16 K and V rows go
+//    straight from global memory to LDS (16-byte direct loads, no registers); both
+//    are stored row-major with an XOR swizzle of their 16-byte chunks.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as A, Q from registers
 //    as B). In the 32x32 accumulator a lane owns one query column and 16 key rows;
-//    the same registers, rounded to bf16, are the B operand of O^T = V^T P^T, once
-//    the keys of V^T are laid out in the order the accumulator holds them (bits 2
-//    and 3 of the key index swapped). O^T also leaves each lane with one query, so
-//    the row max, row sum and rescale never leave the lane pair (l, l^32).
+//    the same registers, rounded to bf16, are the B operand of O^T = V^T P^T. Its A
+//    operand (V^T) is read from row-major V with the LDS transpose read
+//    (ds_read_b64_tr_b16: a 16-lane group reads a 4-key x 16-column block and each
+//    lane receives the 4 keys of one column), two reads per operand, choosing the key
+//    rows so the operand's k order matches the order the accumulator holds the keys
+//    in. O^T also leaves each lane with one query, so the row max, row sum and
+//    rescale never leave the lane pair (l, l^32).
 //  * Online softmax in base 2; the running max is only raised when a row's max
 //    grows by more than 2^8, which keeps every P <= 256 and skips most rescales.
 #include "psa_device.h"
@@ -37,19 +39,8 @@
 
 namespace psa {
 
-// Position of key kappa (0..63) of a tile inside a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int kappa) {
-  return (kappa & 0x33) | ((kappa & 4) << 1) | ((kappa & 8) >> 1);
-}
-
-// Raw global data of 8 consecutive d values of one key row.
-template <typename T> struct Raw8;
-template <> struct Raw8<bf16_t> {
-  U128 r;
-  __device__ __forceinline__ void load(const bf16_t* p) { r = ld128(p); }
-  __device__ __forceinline__ U128 bf16() const { return r; }
-};
-template <> struct Raw8<float> {
+// Raw global data of 8 consecutive d values of one key row (float32 I/O path only).
+struct Raw8f {
   U128 r[2];
   __device__ __forceinline__ void load(const float* p) { r[0] = ld128(p); r[1] = ld128(p + 4); }
   __device__ __forceinline__ U128 bf16() const {
@@ -63,32 +54,48 @@ template <> struct Raw8<float> {
   }
 };
 
-template <typename T, int D, int NW>
+template <int D, int NW>
 struct AttnCfg {
   static constexpr int kThreads = NW * 64;
-  static constexpr int kCpr = D / 8;                // 16-byte bf16 chunks per K row
-  static constexpr int kKpt = kCpr / NW;            // consecutive keys one thread stages
+  static constexpr int kCpr = D / 8;                // 16-byte chunks per 64-row tile row (bf16)
+  static constexpr int kRpb = 64 / kCpr;            // rows per 1 KB block (one wave-wide 16 B load)
+  static constexpr int kBlocks = 64 / kRpb;         // 1 KB blocks per tile and tensor
+  static constexpr int kBpw = kBlocks / NW;         // blocks each wave stages per tensor
   static constexpr int kDt = D / 32;                // 32-wide d blocks of O^T
   static constexpr int kQc = D / 16;                // 16-deep d chunks of Q K^T
-  static_assert(kKpt == 2 || kKpt == 4 || kKpt == 8, "staging layout");
+  static_assert(kBpw >= 1 && kBlocks % NW == 0, "staging layout");
 };
 
-__device__ __forceinline__ int k_swz(int row, int cpr) {
-  return cpr == 16 ? (row & 15) : ((row >> 1) & 7);
+// LDS tiles are row-major [64 keys][D] bf16 with the 16-byte chunks of row r XOR-ed by a
+// row-dependent mask. For K the mask spreads the 16 rows one 128-bit operand read
+// touches over distinct banks; for V it spreads the 4 rows x 32 bytes that one
+// 16-lane group of a transposing read touches. Both are permutations within a row,
+// so a wave-wide direct load of whole rows stays conflict-free.
+template <int D> __device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
 template <typename T, int D, int NW>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                         const T* __restrict__ kp, const T* __restrict__ vp,
                         const int8_t* __restrict__ level_map, T* __restrict__ o, float* __restrict__ lse,
                         int H, int H_kv, int N, int nqb, int nkb, int L, int total_items, int per_xcd,
                         int64_t pyr_rows, int off1, int off2, int off3, int rows1, int rows2, int rows3,
                         float cs /* scale * log2(e) */) {
-  using C = AttnCfg<T, D, NW>;
-  constexpr int CPR = C::kCpr, KPT = C::kKpt;
+  using C = AttnCfg<D, NW>;
+  constexpr int CPR = C::kCpr, RPB = C::kRpb, BPW = C::kBpw;
+  constexpr bool kDirect = sizeof(T) == 2;     // bf16: global -> LDS without registers
   __shared__ __align__(16) uint16_t Ks[2][64 * D];
-  __shared__ __align__(16) uint16_t Vt[2][D * 64];
+  __shared__ __align__(16) uint16_t Vs[2][64 * D];
   __shared__ float corr[2][64];
   __shared__ int16_t blist[kMaxKvBlocks];
   __shared__ int s_cnt[4], s_start[4], s_tile[5];
@@ -153,121 +160,110 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const T* qrow = q + ((int64_t)bh * N + min(my_row, N - 1)) * D;
 #pragma unroll
     for (int c = 0; c < C::kQc; ++c) {
-      Raw8<T> rw;
-      rw.load(qrow + 16 * c + 8 * half);
-      U128 u = rw.bf16();
+      U128 u;
+      if constexpr (kDirect) {
+        u = ld128(qrow + 16 * c + 8 * half);
+      } else {
+        Raw8f rw;
+        rw.load(reinterpret_cast<const float*>(qrow) + 16 * c + 8 * half);
+        u = rw.bf16();
+      }
       if (my_row >= N) u = U128{{0u, 0u, 0u, 0u}};
       qreg[c] = __builtin_bit_cast(bf16x8, make_uint4(u.w[0], u.w[1], u.w[2], u.w[3]));
     }
   }
+  // Retire the Q loads here: otherwise the wait-count analysis cannot prove them done
+  // inside the tile loop and waits on every outstanding load (the next tile's prefetch)
+  // before each QK^T product. 0x0F70 = vmcnt(0), expcnt and lgkmcnt unconstrained.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  const int T_total = s_tile[4];
+  // per-level tile bookkeeping, wave-uniform
+  int t_start[5], l_cnt[4], l_start[4];
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    t_start[l] = __builtin_amdgcn_readfirstlane(s_tile[l]);
+    l_cnt[l] = __builtin_amdgcn_readfirstlane(s_cnt[l]);
+    l_start[l] = __builtin_amdgcn_readfirstlane(s_start[l]);
+  }
+  t_start[4] = __builtin_amdgcn_readfirstlane(s_tile[4]);
+  const int T_total = t_start[4];
+  const int rem = N & 63;
+  bool tail_in[4];
+#pragma unroll
+  for (int l = 0; l < 4; ++l)
+    tail_in[l] = rem != 0 && l_cnt[l] > 0 && blist[l_start[l] + l_cnt[l] - 1] == nkb - 1;
+
   const T* kh = k + (int64_t)bkv * N * D;
   const T* vh = v + (int64_t)bkv * N * D;
   const T* kph = kp ? kp + (int64_t)bkv * pyr_rows * D : nullptr;
   const T* vph = vp ? vp + (int64_t)bkv * pyr_rows * D : nullptr;
   const int offs[4] = {0, off1, off2, off3};
   const int rows_l[4] = {N, rows1, rows2, rows3};
-  const int rem = N & 63;
 
-  // staging role: 16-byte chunk sc of keys KPT*sg .. KPT*sg + KPT-1
-  const int sc = tid % CPR, sg = tid / CPR;
-  const int key0 = KPT * sg;
-
-  // tile t -> (level, index within level, irregular?)
-  auto tile_info = [&](int t, int& lvl, int& u, bool& irregular) {
+  // tile t -> level, index within the level, irregular (padding or ragged tail: per-key fixups)
+  auto tile_info = [&](int t, int& lvl, int& u, bool& irr) {
     lvl = 0;
 #pragma unroll
     for (int l = 1; l < 4; ++l)
-      if (t >= s_tile[l]) lvl = l;
-    u = t - s_tile[lvl];
-    const int cntl = s_cnt[lvl];
-    const int ntl = s_tile[lvl + 1] - s_tile[lvl];
-    const bool last = (u == ntl - 1);
-    const bool pad = (cntl & ((1 << lvl) - 1)) != 0;
-    const bool tail = rem != 0 && blist[s_start[lvl] + cntl - 1] == nkb - 1;
-    irregular = last && (pad || tail);
+      if (t >= t_start[l]) lvl = l;
+    u = t - t_start[lvl];
+    const bool last = t == t_start[lvl + 1] - 1;
+    irr = last && (((l_cnt[lvl] & ((1 << lvl) - 1)) != 0) || tail_in[lvl]);
   };
 
-  Raw8<T> kr[KPT], vr[KPT];
-  auto load_tile = [&](int t) {
+  // Staging: wave w fills 1 KB blocks w*BPW .. w*BPW+BPW-1 of each tensor's tile; in a
+  // block, lane i owns row RPB*blk + i/CPR and physical chunk i%CPR.
+  const int st_row0 = RPB * (wave * BPW) + lane / CPR;
+  const int st_pchunk = lane % CPR;
+  Raw8f fk[kDirect ? 1 : BPW], fv[kDirect ? 1 : BPW];
+  auto issue_tile = [&](int t, int buf) {
     int lvl, u; bool irr;
     tile_info(t, lvl, u, irr);
-    const int seglen = 64 >> lvl;
-    const int li = (u << lvl) + (key0 >> (6 - lvl));
-    const bool vseg = li < s_cnt[lvl];
-    const int blk = vseg ? (int)blist[s_start[lvl] + li] : 0;
-    const int prow0 = blk * seglen + (key0 & (seglen - 1));
+    const int sh = 6 - lvl, seglen = 64 >> lvl;
     const T* kb = lvl == 0 ? kh : kph + (int64_t)offs[lvl] * D;
     const T* vb = lvl == 0 ? vh : vph + (int64_t)offs[lvl] * D;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int prow = prow0 + i;
+    for (int i = 0; i < BPW; ++i) {
+      const int row = st_row0 + RPB * i;
+      const int li = (u << lvl) + (row >> sh);
+      const bool vseg = li < l_cnt[lvl];
+      const int blk = vseg ? (int)blist[l_start[lvl] + li] : 0;
+      const int prow = blk * seglen + (row & (seglen - 1));
       const bool ok = vseg && prow < rows_l[lvl];
-      const int64_t r = ok ? prow : 0;
-      kr[i].load(kb + r * D + 8 * sc);
-      vr[i].load(vb + r * D + 8 * sc);
-    }
-  };
-  auto store_tile = [&](int t, int buf) {
-    int lvl, u; bool irr;
-    tile_info(t, lvl, u, irr);
-    uint16_t* kd = Ks[buf];
-    uint16_t* vd = Vt[buf];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int row = key0 + i;
-      const U128 x = kr[i].bf16();
-      st128(kd + row * D + ((sc ^ k_swz(row, CPR)) * 8), x);
-    }
-    U128 xv[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) xv[i] = vr[i].bf16();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * sc + e;
-      const int w = e >> 1;
-      const bool hi = e & 1;
-      uint16_t* vrow = vd + d * 64;
-      const int swz = (d >> 1) & 7;
-      if constexpr (KPT == 2) {
-        const uint32_t a = xv[0].w[w], c = xv[1].w[w];
-        const uint32_t pk = hi ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
-        const int pos = vt_pos(key0);
-        *reinterpret_cast<uint32_t*>(vrow + (((pos >> 3) ^ swz) * 8) + (pos & 7)) = pk;
+      const int64_t goff = (int64_t)(ok ? prow : 0) * D;
+      if constexpr (kDirect) {
+        const int blkoff = (wave * BPW + i) * 512;    // 1 KB block, in bf16 elements
+        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + goff + 8 * (st_pchunk ^ k_swz<D>(row))),
+                                         (lds_void*)(Ks[buf] + blkoff), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + goff + 8 * (st_pchunk ^ v_swz<D>(row))),
+                                         (lds_void*)(Vs[buf] + blkoff), 16, 0, 0);
       } else {
-#pragma unroll
-        for (int g4 = 0; g4 < KPT / 4; ++g4) {
-          const uint32_t a0 = xv[4 * g4].w[w], a1 = xv[4 * g4 + 1].w[w];
-          const uint32_t a2 = xv[4 * g4 + 2].w[w], a3 = xv[4 * g4 + 3].w[w];
-          uint2 pk;
-          pk.x = hi ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-          pk.y = hi ? ((a2 >> 16) | (a3 & 0xffff0000u)) : ((a2 & 0xffffu) | (a3 << 16));
-          const int pos = vt_pos(key0 + 4 * g4);
-          *reinterpret_cast<uint2*>(vrow + (((pos >> 3) ^ swz) * 8) + (pos & 7)) = pk;
-        }
+        fk[i].load(reinterpret_cast<const float*>(kb + goff) + 8 * (st_pchunk ^ k_swz<D>(row)));
+        fv[i].load(reinterpret_cast<const float*>(vb + goff) + 8 * (st_pchunk ^ v_swz<D>(row)));
       }
-    }
-    if (irr && sc == 0) {
-      // per-key logit correction (in units of the raw dot product):
-      // -inf for padding / rows past the sequence, log2(c)-l for a ragged pool group
-      const int seglen = 64 >> lvl;
-      const int li = (u << lvl) + (key0 >> (6 - lvl));
-      const bool vseg = li < s_cnt[lvl];
-      const int blk = vseg ? (int)blist[s_start[lvl] + li] : 0;
-      const int prow0 = blk * seglen + (key0 & (seglen - 1));
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int prow = prow0 + i;
+      if (irr && st_pchunk == 0) {
+        // per-key logit correction, in units of the raw dot product: -inf for padding and
+        // rows past the sequence, (log2 c - l)/cs for a ragged pool group of c tokens
         float cval = -INFINITY;
-        if (vseg && prow < rows_l[lvl]) {
+        if (ok) {
           const int cnt = min(1 << lvl, N - (prow << lvl));
           cval = cnt == (1 << lvl) ? 0.f : (__log2f((float)cnt) - (float)lvl) / cs;
         }
-        corr[buf][key0 + i] = cval;
+        corr[buf][row] = cval;
       }
     }
+  };
+  auto commit_tile = [&](int buf) {
+    if constexpr (!kDirect) {
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int off = (wave * BPW + i) * 512 + lane * 8;
+        st128(Ks[buf] + off, fk[i].bf16());
+        st128(Vs[buf] + off, fv[i].bf16());
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's direct-to-LDS loads have landed
   };
 
   f32x16 oacc[C::kDt];
@@ -278,18 +274,25 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   float m_run = -INFINITY, l_run = 0.f;
 
   if (T_total > 0) {
-    load_tile(0);
-    store_tile(0, 0);
+    issue_tile(0, 0);
+    commit_tile(0);
   }
   __syncthreads();
 
+  // V operand addressing for ds_read_b64_tr_b16: in 16-lane group G, lane 4m+q points at
+  // key row (16c + 8j + 4*(G/2) + m), columns 32tt + 16*(G%2) + 4q .. +3; the group then
+  // holds, per lane, 4 consecutive keys of one d column.
+  const int trg = lane >> 4, trs = lane & 15;
+  const int tr_row = 4 * (trg >> 1) + (trs >> 2);
+  const int tr_col = 16 * (trg & 1) + 4 * (trs & 3);
+
   for (int t = 0; t < T_total; ++t) {
     const int buf = t & 1;
-    if (t + 1 < T_total) load_tile(t + 1);
+    if (t + 1 < T_total) issue_tile(t + 1, buf ^ 1);
     int lvl, u; bool irr;
     tile_info(t, lvl, u, irr);
     const uint16_t* Kb = Ks[buf];
-    const uint16_t* Vb = Vt[buf];
+    const uint16_t* Vb = Vs[buf];
 
     // S^T = K Q^T: two 32-key halves
     f32x16 sacc[2];
@@ -299,7 +302,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       for (int x = 0; x < 16; ++x) sacc[kb][x] = 0.f;
       const int krow = 32 * kb + l32;
       const uint16_t* kr_l = Kb + krow * D;
-      const int swz = k_swz(krow, CPR);
+      const int swz = k_swz<D>(krow);
 #pragma unroll
       for (int c = 0; c < C::kQc; ++c) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr_l + (((2 * c + half) ^ swz) * 8));
@@ -348,20 +351,26 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     }
     l_run += lsum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; the A operand is fetched transposed from row-major V
 #pragma unroll
     for (int tt = 0; tt < C::kDt; ++tt) {
-      const int drow = 32 * tt + l32;
-      const uint16_t* vr_l = Vb + drow * 64;
-      const int swz = (drow >> 1) & 7;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vr_l + (((2 * c + half) ^ swz) * 8));
+        bf16x4 part[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = 16 * c + 8 * j + tr_row;
+          const int col = 32 * tt + tr_col;
+          const int chunk = (col >> 3) ^ v_swz<D>(row);
+          part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(Vb + row * D + chunk * 8 + (col & 7)));
+        }
+        const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, preg[c], oacc[tt], 0, 0, 0);
       }
     }
 
-    if (t + 1 < T_total) store_tile(t + 1, buf ^ 1);
+    if (t + 1 < T_total) commit_tile(buf ^ 1);
     __syncthreads();
   }
 
