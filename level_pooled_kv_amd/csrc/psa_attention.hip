@@ -89,8 +89,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
                         const T* __restrict__ kp, const T* __restrict__ vp,
                         const int8_t* __restrict__ level_map, T* __restrict__ o, float* __restrict__ lse,
                         int H, int H_kv, int N, int nqb, int nkb, int L, int total_items, int per_xcd,
-                        int64_t pyr_rows, int off1, int off2, int off3, int rows1, int rows2, int rows3,
-                        float cs /* scale * log2(e) */) {
+                        int64_t pyr_rows, int rows1, int rows2, float cs /* scale * log2(e) */) {
   using C = AttnCfg<D, NW>;
   constexpr int CPR = C::kCpr, RPB = C::kRpb, BPW = C::kBpw;
   constexpr bool kDirect = sizeof(T) == 2;     // bf16: global -> LDS without registers
@@ -98,7 +97,8 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   __shared__ __align__(16) uint16_t Vs[2][64 * D];
   __shared__ float corr[2][64];
   __shared__ int16_t blist[kMaxKvBlocks];
-  __shared__ int s_cnt[4], s_start[4], s_tile[5];
+  __shared__ uint32_t tdesc[kMaxKvBlocks + 4];   // per tile: level | list base << 2 | segs << 16 | irregular << 31
+  __shared__ int s_tile[5];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bid = blockIdx.x;
@@ -123,16 +123,14 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     pos[0] = 0;
 #pragma unroll
     for (int l = 1; l < 4; ++l) pos[l] = pos[l - 1] + cnt[l - 1];
-    if (lane == 0) {
-      int ts = 0;
+    const int start[4] = {pos[0], pos[1], pos[2], pos[3]};
+    int tfirst[5];
+    tfirst[0] = 0;
 #pragma unroll
-      for (int l = 0; l < 4; ++l) {
-        s_cnt[l] = cnt[l];
-        s_start[l] = pos[l];
-        s_tile[l] = ts;
-        ts += (cnt[l] + (1 << l) - 1) >> l;
-      }
-      s_tile[4] = ts;
+    for (int l = 0; l < 4; ++l) tfirst[l + 1] = tfirst[l] + ((cnt[l] + (1 << l) - 1) >> l);
+    if (lane == 0) {
+#pragma unroll
+      for (int l = 0; l < 5; ++l) s_tile[l] = tfirst[l];
     }
     for (int j0 = 0; j0 < nkb; j0 += 64) {
       const int j = j0 + lane;
@@ -147,6 +145,20 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
           blist[pos[l] + below] = (int16_t)j;
         }
         pos[l] += __popcll(m);
+      }
+    }
+    // Tile descriptors. A tile is irregular (needs per-key fixups) when it is the last of
+    // its level and has padding segments or holds the ragged final KV block.
+    const int rem = N & 63;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int ntl = tfirst[l + 1] - tfirst[l];
+      const bool tail = rem != 0 && cnt[l] > 0 && blist[start[l] + cnt[l] - 1] == nkb - 1;
+      for (int u = lane; u < ntl; u += 64) {
+        const int nseg = min(1 << l, cnt[l] - (u << l));
+        const bool irr = u == ntl - 1 && (nseg < (1 << l) || tail);
+        tdesc[tfirst[l] + u] = (uint32_t)l | ((uint32_t)(start[l] + (u << l)) << 2) | ((uint32_t)nseg << 16) |
+                               (irr ? 0x80000000u : 0u);
       }
     }
   }
@@ -178,39 +190,21 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  // per-level tile bookkeeping, wave-uniform
-  int t_start[5], l_cnt[4], l_start[4];
-#pragma unroll
-  for (int l = 0; l < 4; ++l) {
-    t_start[l] = __builtin_amdgcn_readfirstlane(s_tile[l]);
-    l_cnt[l] = __builtin_amdgcn_readfirstlane(s_cnt[l]);
-    l_start[l] = __builtin_amdgcn_readfirstlane(s_start[l]);
-  }
-  t_start[4] = __builtin_amdgcn_readfirstlane(s_tile[4]);
-  const int T_total = t_start[4];
-  const int rem = N & 63;
-  bool tail_in[4];
-#pragma unroll
-  for (int l = 0; l < 4; ++l)
-    tail_in[l] = rem != 0 && l_cnt[l] > 0 && blist[l_start[l] + l_cnt[l] - 1] == nkb - 1;
+  const int T_total = __builtin_amdgcn_readfirstlane(s_tile[4]);
 
   const T* kh = k + (int64_t)bkv * N * D;
   const T* vh = v + (int64_t)bkv * N * D;
   const T* kph = kp ? kp + (int64_t)bkv * pyr_rows * D : nullptr;
   const T* vph = vp ? vp + (int64_t)bkv * pyr_rows * D : nullptr;
-  const int offs[4] = {0, off1, off2, off3};
-  const int rows_l[4] = {N, rows1, rows2, rows3};
-
-  // tile t -> level, index within the level, irregular (padding or ragged tail: per-key fixups)
-  auto tile_info = [&](int t, int& lvl, int& u, bool& irr) {
-    lvl = 0;
-#pragma unroll
-    for (int l = 1; l < 4; ++l)
-      if (t >= t_start[l]) lvl = l;
-    u = t - t_start[lvl];
-    const bool last = t == t_start[lvl + 1] - 1;
-    irr = last && (((l_cnt[lvl] & ((1 << lvl) - 1)) != 0) || tail_in[lvl]);
+  // tile t -> level, first block-list index, valid segments, irregular flag
+  struct TileInfo { int lvl, base, nseg; bool irr; };
+  auto tile_info = [&](int t) {
+    const uint32_t d = __builtin_amdgcn_readfirstlane(tdesc[t]);
+    return TileInfo{(int)(d & 3u), (int)((d >> 2) & 0x3fffu), (int)((d >> 16) & 15u), (d >> 31) != 0};
   };
+  // per-level constants: pooled rows, row offset in the pyramid, K/V base pointers
+  auto level_rows = [&](int lvl) { return (N + (1 << lvl) - 1) >> lvl; };
+  auto level_off = [&](int lvl) { return (lvl >= 2 ? rows1 : 0) + (lvl >= 3 ? rows2 : 0); };
 
   // Staging: wave w fills 1 KB blocks w*BPW .. w*BPW+BPW-1 of each tensor's tile; in a
   // block, lane i owns row RPB*blk + i/CPR and physical chunk i%CPR.
@@ -218,19 +212,21 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   const int st_pchunk = lane % CPR;
   Raw8f fk[kDirect ? 1 : BPW], fv[kDirect ? 1 : BPW];
   auto issue_tile = [&](int t, int buf) {
-    int lvl, u; bool irr;
-    tile_info(t, lvl, u, irr);
+    const TileInfo ti = tile_info(t);
+    const int lvl = ti.lvl;
     const int sh = 6 - lvl, seglen = 64 >> lvl;
-    const T* kb = lvl == 0 ? kh : kph + (int64_t)offs[lvl] * D;
-    const T* vb = lvl == 0 ? vh : vph + (int64_t)offs[lvl] * D;
+    const int rows_lv = level_rows(lvl);
+    const int64_t loff = (int64_t)level_off(lvl) * D;
+    const T* kb = lvl == 0 ? kh : kph + loff;
+    const T* vb = lvl == 0 ? vh : vph + loff;
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int row = st_row0 + RPB * i;
-      const int li = (u << lvl) + (row >> sh);
-      const bool vseg = li < l_cnt[lvl];
-      const int blk = vseg ? (int)blist[l_start[lvl] + li] : 0;
+      const int seg = row >> sh;
+      const bool vseg = seg < ti.nseg;
+      const int blk = vseg ? (int)blist[ti.base + seg] : 0;
       const int prow = blk * seglen + (row & (seglen - 1));
-      const bool ok = vseg && prow < rows_l[lvl];
+      const bool ok = vseg && prow < rows_lv;
       const int64_t goff = (int64_t)(ok ? prow : 0) * D;
       if constexpr (kDirect) {
         const int blkoff = (wave * BPW + i) * 512;    // 1 KB block, in bf16 elements
@@ -242,7 +238,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         fk[i].load(reinterpret_cast<const float*>(kb + goff) + 8 * (st_pchunk ^ k_swz<D>(row)));
         fv[i].load(reinterpret_cast<const float*>(vb + goff) + 8 * (st_pchunk ^ v_swz<D>(row)));
       }
-      if (irr && st_pchunk == 0) {
+      if (ti.irr && st_pchunk == 0) {
         // per-key logit correction, in units of the raw dot product: -inf for padding and
         // rows past the sequence, (log2 c - l)/cs for a ragged pool group of c tokens
         float cval = -INFINITY;
@@ -289,8 +285,9 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   for (int t = 0; t < T_total; ++t) {
     const int buf = t & 1;
     if (t + 1 < T_total) issue_tile(t + 1, buf ^ 1);
-    int lvl, u; bool irr;
-    tile_info(t, lvl, u, irr);
+    const TileInfo ti = tile_info(t);
+    const int lvl = ti.lvl;
+    const bool irr = ti.irr;
     const uint16_t* Kb = Ks[buf];
     const uint16_t* Vb = Vs[buf];
 
@@ -323,7 +320,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sacc[kb][x]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    {   // lanes l and l^32 hold the two key halves of one query
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float lvlf = (float)lvl;
     const float mt = fmaf(tmax, cs, lvlf);
     const bool upd = mt > m_run + 8.0f;
@@ -375,7 +375,8 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   }
 
   // ---- normalise and write O (and LSE)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (my_row < N) {
     T* orow = o + ((int64_t)bh * N + my_row) * D;
@@ -407,7 +408,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                      static_cast<const T*>(a.k_pyr), static_cast<const T*>(a.v_pyr), a.level_map,
                      static_cast<T*>(a.o), a.lse, a.H, a.H_kv, a.N, a.nqb, a.nkb, a.L, total, per,
-                     a.pyr_rows, a.off[1], a.off[2], a.off[3], a.rows[1], a.rows[2], a.rows[3], cs);
+                     a.pyr_rows, a.rows[1], a.rows[2], cs);
   return hipGetLastError();
 }
 
