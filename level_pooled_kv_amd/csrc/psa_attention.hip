@@ -34,54 +34,11 @@
 //    rescale never leave the lane pair (l, l^32).
 //  * Online softmax in base 2; the running max is only raised when a row's max
 //    grows by more than 2^8, which keeps every P <= 256 and skips most rescales.
-#include "psa_device.h"
-#include "psa_launch.h"
+#include "psa_attn_common.h"
+
+#include <type_traits>
 
 namespace psa {
-
-// Raw global data of 8 consecutive d values of one key row (float32 I/O path only).
-struct Raw8f {
-  U128 r[2];
-  __device__ __forceinline__ void load(const float* p) { r[0] = ld128(p); r[1] = ld128(p + 4); }
-  __device__ __forceinline__ U128 bf16() const {
-    U128 o;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      o.w[2 * i] = pack_bf16x2(__uint_as_float(r[i].w[0]), __uint_as_float(r[i].w[1]));
-      o.w[2 * i + 1] = pack_bf16x2(__uint_as_float(r[i].w[2]), __uint_as_float(r[i].w[3]));
-    }
-    return o;
-  }
-};
-
-template <int D, int NW>
-struct AttnCfg {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kCpr = D / 8;                // 16-byte chunks per 64-row tile row (bf16)
-  static constexpr int kRpb = 64 / kCpr;            // rows per 1 KB block (one wave-wide 16 B load)
-  static constexpr int kBlocks = 64 / kRpb;         // 1 KB blocks per tile and tensor
-  static constexpr int kBpw = kBlocks / NW;         // blocks each wave stages per tensor
-  static constexpr int kDt = D / 32;                // 32-wide d blocks of O^T
-  static constexpr int kQc = D / 16;                // 16-deep d chunks of Q K^T
-  static_assert(kBpw >= 1 && kBlocks % NW == 0, "staging layout");
-};
-
-// LDS tiles are row-major [64 keys][D] bf16 with the 16-byte chunks of row r XOR-ed by a
-// row-dependent mask. For K the mask spreads the 16 rows one 128-bit operand read
-// touches over distinct banks; for V it spreads the 4 rows x 32 bytes that one
-// 16-lane group of a transposing read touches. Both are permutations within a row,
-// so a wave-wide direct load of whole rows stays conflict-free.
-template <int D> __device__ __forceinline__ int k_swz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D> __device__ __forceinline__ int v_swz(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <typename T, int D, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -93,8 +50,11 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   using C = AttnCfg<D, NW>;
   constexpr int CPR = C::kCpr, RPB = C::kRpb, BPW = C::kBpw;
   constexpr bool kDirect = sizeof(T) == 2;     // bf16: global -> LDS without registers
-  __shared__ __align__(16) uint16_t Ks[2][64 * D];
-  __shared__ __align__(16) uint16_t Vs[2][64 * D];
+  // One LDS object per tile buffer: the wait-count analysis can then tell the direct
+  // loads into one buffer from the operand reads of the other and does not make the
+  // reads wait for the prefetch. Buffer choices are therefore compile-time (parity P).
+  __shared__ __align__(16) uint16_t K0[64 * D], K1[64 * D];
+  __shared__ __align__(16) uint16_t V0[64 * D], V1[64 * D];
   __shared__ float corr[2][64];
   __shared__ int16_t blist[kMaxKvBlocks];
   __shared__ uint32_t tdesc[kMaxKvBlocks + 4];   // per tile: level | list base << 2 | segs << 16 | irregular << 31
@@ -110,58 +70,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 
   // ---- compact the level-map row into level-major block lists (wave 0)
   const int8_t* lrow = level_map + (int64_t)item * nkb;   // item == (b*H + h)*nqb + qi
-  if (wave == 0) {
-    int cnt[4] = {0, 0, 0, 0};
-    for (int j0 = 0; j0 < nkb; j0 += 64) {
-      const int j = j0 + lane;
-      int lev = j < nkb ? (int)lrow[j] : -1;
-      if (lev >= L) lev = -1;
-#pragma unroll
-      for (int l = 0; l < 4; ++l) cnt[l] += __popcll(__ballot(lev == l));
-    }
-    int pos[4];
-    pos[0] = 0;
-#pragma unroll
-    for (int l = 1; l < 4; ++l) pos[l] = pos[l - 1] + cnt[l - 1];
-    const int start[4] = {pos[0], pos[1], pos[2], pos[3]};
-    int tfirst[5];
-    tfirst[0] = 0;
-#pragma unroll
-    for (int l = 0; l < 4; ++l) tfirst[l + 1] = tfirst[l] + ((cnt[l] + (1 << l) - 1) >> l);
-    if (lane == 0) {
-#pragma unroll
-      for (int l = 0; l < 5; ++l) s_tile[l] = tfirst[l];
-    }
-    for (int j0 = 0; j0 < nkb; j0 += 64) {
-      const int j = j0 + lane;
-      int lev = j < nkb ? (int)lrow[j] : -1;
-      if (lev >= L) lev = -1;
-#pragma unroll
-      for (int l = 0; l < 4; ++l) {
-        const uint64_t m = __ballot(lev == l);
-        if (lev == l) {
-          const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-          blist[pos[l] + below] = (int16_t)j;
-        }
-        pos[l] += __popcll(m);
-      }
-    }
-    // Tile descriptors. A tile is irregular (needs per-key fixups) when it is the last of
-    // its level and has padding segments or holds the ragged final KV block.
-    const int rem = N & 63;
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      const int ntl = tfirst[l + 1] - tfirst[l];
-      const bool tail = rem != 0 && cnt[l] > 0 && blist[start[l] + cnt[l] - 1] == nkb - 1;
-      for (int u = lane; u < ntl; u += 64) {
-        const int nseg = min(1 << l, cnt[l] - (u << l));
-        const bool irr = u == ntl - 1 && (nseg < (1 << l) || tail);
-        tdesc[tfirst[l] + u] = (uint32_t)l | ((uint32_t)(start[l] + (u << l)) << 2) | ((uint32_t)nseg << 16) |
-                               (irr ? 0x80000000u : 0u);
-      }
-    }
-  }
+  if (wave == 0) build_tile_lists(lrow, nkb, L, N, blist, tdesc, s_tile);
 
   // ---- Q operand in registers: lane (row = lane%32, half = lane/32) holds d = 16c + 8*half + 0..7
   const int half = lane >> 5, l32 = lane & 31;
@@ -197,11 +106,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   const T* kph = kp ? kp + (int64_t)bkv * pyr_rows * D : nullptr;
   const T* vph = vp ? vp + (int64_t)bkv * pyr_rows * D : nullptr;
   // tile t -> level, first block-list index, valid segments, irregular flag
-  struct TileInfo { int lvl, base, nseg; bool irr; };
-  auto tile_info = [&](int t) {
-    const uint32_t d = __builtin_amdgcn_readfirstlane(tdesc[t]);
-    return TileInfo{(int)(d & 3u), (int)((d >> 2) & 0x3fffu), (int)((d >> 16) & 15u), (d >> 31) != 0};
-  };
+  auto tile_info = [&](int t) { return decode_tile(__builtin_amdgcn_readfirstlane(tdesc[t])); };
   // per-level constants: pooled rows, row offset in the pyramid, K/V base pointers
   auto level_rows = [&](int lvl) { return (N + (1 << lvl) - 1) >> lvl; };
   auto level_off = [&](int lvl) { return (lvl >= 2 ? rows1 : 0) + (lvl >= 3 ? rows2 : 0); };
@@ -211,7 +116,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   const int st_row0 = RPB * (wave * BPW) + lane / CPR;
   const int st_pchunk = lane % CPR;
   Raw8f fk[kDirect ? 1 : BPW], fv[kDirect ? 1 : BPW];
-  auto issue_tile = [&](int t, int buf) {
+  auto kbuf = [&](auto P) -> uint16_t* { if constexpr (P() == 0) return K0; else return K1; };
+  auto vbuf = [&](auto P) -> uint16_t* { if constexpr (P() == 0) return V0; else return V1; };
+  auto issue_tile = [&](int t, auto P) {
+    constexpr int buf = P();
     const TileInfo ti = tile_info(t);
     const int lvl = ti.lvl;
     const int sh = 6 - lvl, seglen = 64 >> lvl;
@@ -231,35 +139,25 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       if constexpr (kDirect) {
         const int blkoff = (wave * BPW + i) * 512;    // 1 KB block, in bf16 elements
         __builtin_amdgcn_global_load_lds((gbl_void*)(kb + goff + 8 * (st_pchunk ^ k_swz<D>(row))),
-                                         (lds_void*)(Ks[buf] + blkoff), 16, 0, 0);
+                                         (lds_void*)(kbuf(P) + blkoff), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((gbl_void*)(vb + goff + 8 * (st_pchunk ^ v_swz<D>(row))),
-                                         (lds_void*)(Vs[buf] + blkoff), 16, 0, 0);
+                                         (lds_void*)(vbuf(P) + blkoff), 16, 0, 0);
       } else {
         fk[i].load(reinterpret_cast<const float*>(kb + goff) + 8 * (st_pchunk ^ k_swz<D>(row)));
         fv[i].load(reinterpret_cast<const float*>(vb + goff) + 8 * (st_pchunk ^ v_swz<D>(row)));
       }
-      if (ti.irr && st_pchunk == 0) {
-        // per-key logit correction, in units of the raw dot product: -inf for padding and
-        // rows past the sequence, (log2 c - l)/cs for a ragged pool group of c tokens
-        float cval = -INFINITY;
-        if (ok) {
-          const int cnt = min(1 << lvl, N - (prow << lvl));
-          cval = cnt == (1 << lvl) ? 0.f : (__log2f((float)cnt) - (float)lvl) / cs;
-        }
-        corr[buf][row] = cval;
-      }
+      if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
     }
   };
-  auto commit_tile = [&](int buf) {
+  auto commit_tile = [&](auto P) {
     if constexpr (!kDirect) {
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
         const int off = (wave * BPW + i) * 512 + lane * 8;
-        st128(Ks[buf] + off, fk[i].bf16());
-        st128(Vs[buf] + off, fv[i].bf16());
+        st128(kbuf(P) + off, fk[i].bf16());
+        st128(vbuf(P) + off, fv[i].bf16());
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's direct-to-LDS loads have landed
   };
 
   f32x16 oacc[C::kDt];
@@ -269,9 +167,11 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     for (int x = 0; x < 16; ++x) oacc[t][x] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   if (T_total > 0) {
-    issue_tile(0, 0);
-    commit_tile(0);
+    issue_tile(0, P0{});
+    commit_tile(P0{});
   }
   __syncthreads();
 
@@ -282,14 +182,16 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   const int tr_row = 4 * (trg >> 1) + (trs >> 2);
   const int tr_col = 16 * (trg & 1) + 4 * (trs & 3);
 
-  for (int t = 0; t < T_total; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < T_total) issue_tile(t + 1, buf ^ 1);
+  // tile t (t % 2 == P()): prefetch tile t+1 into the other buffers, then compute t
+  auto body = [&](int t, auto P) {
+    constexpr int buf = P();
+    using PN = std::integral_constant<int, 1 - P()>;
+    if (t + 1 < T_total) issue_tile(t + 1, PN{});
     const TileInfo ti = tile_info(t);
     const int lvl = ti.lvl;
     const bool irr = ti.irr;
-    const uint16_t* Kb = Ks[buf];
-    const uint16_t* Vb = Vs[buf];
+    const uint16_t* Kb = kbuf(P);
+    const uint16_t* Vb = vbuf(P);
 
     // S^T = K Q^T: two 32-key halves
     f32x16 sacc[2];
@@ -370,8 +272,13 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       }
     }
 
-    if (t + 1 < T_total) commit_tile(buf ^ 1);
+    if (t + 1 < T_total) commit_tile(PN{});
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of tile t+1 have landed
     __syncthreads();
+  };
+  for (int t = 0; t < T_total; t += 2) {
+    body(t, P0{});
+    if (t + 1 < T_total) body(t + 1, P1{});
   }
 
   // ---- normalise and write O (and LSE)
@@ -421,7 +328,11 @@ static hipError_t launch_attn_dtype(const AttnArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
+#ifdef PSA_ATTN_TWO_GROUP
+  return launch_attention_pp(a, stream);
+#else
   return a.bf16 ? launch_attn_dtype<bf16_t>(a, stream) : launch_attn_dtype<float>(a, stream);
+#endif
 }
 
 }  // namespace psa

@@ -40,6 +40,7 @@ struct AttnArgs {
 
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);      // picks a kernel
+hipError_t launch_attention_pp(const AttnArgs& a, hipStream_t stream);   // two-group kernel
 
 }  // namespace psa
