@@ -31,7 +31,22 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan13b_traffic.txt")
-ATTN_SOURCE = os.path.join(ROOT, "level_pooled_kv_amd", "csrc", "psa_attention.hip")
+ATTN_SOURCES = [os.path.join(ROOT, "level_pooled_kv_amd", "csrc", f)
+                for f in ("psa_attn_common.h", "psa_attention.hip", "psa_attention_pp.hip")]
+
+
+def attention_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def attention_kernel_name(d: int, q_block: int, dtype: str) -> str:
+    t = "bf16" if dtype == "bf16" else "float"
+    if os.environ.get("PSA_ATTENTION_KERNEL") == "pp":
+        return f"pyramid_attn_fwd_pp_kernel<{t},{d},{q_block // 32}>"
+    return f"pyramid_attn_fwd_kernel<{t},{d},{q_block // 32}>"
 
 
 def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, d: int) -> float:
@@ -62,8 +77,7 @@ def traffic_from_profile():
         if "=" in line and not line.lstrip().startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-    if kv.get("attention_source_sha256") != src:
+    if kv.get("attention_source_sha256") != attention_source_hash():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -186,7 +200,7 @@ def main():
                    "num_levels": w.num_levels, "thresholds": list(tau), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "pyramid_attn_fwd_kernel<bf16,128,4>"},
+                     "traffic": traffic, "kernel": attention_kernel_name(w.d, w.q_block, w.dtype)},
         "calls_ms": {"build_pyramid": round(pyr_ms, 4), "estimate_mask": round(mask_ms, 4),
                      "attention_fwd": round(attn_ms, 4)},
         "effective_flops": flops, "flop_fraction_rho": round(rho, 5),

@@ -36,6 +36,9 @@
 //    grows by more than 2^8, which keeps every P <= 256 and skips most rescales.
 #include "psa_attn_common.h"
 
+#include <cstdlib>
+#include <cstring>
+
 #include <type_traits>
 
 namespace psa {
@@ -125,8 +128,9 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const int sh = 6 - lvl, seglen = 64 >> lvl;
     const int rows_lv = level_rows(lvl);
     const int64_t loff = (int64_t)level_off(lvl) * D;
-    const T* kb = lvl == 0 ? kh : kph + loff;
-    const T* vb = lvl == 0 ? vh : vph + loff;
+    // wave-uniform bases of the level + 32-bit per-lane byte offsets (scalar-base addressing)
+    const char* kb = reinterpret_cast<const char*>(lvl == 0 ? kh : kph + loff);
+    const char* vb = reinterpret_cast<const char*>(lvl == 0 ? vh : vph + loff);
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int row = st_row0 + RPB * i;
@@ -135,16 +139,16 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       const int blk = vseg ? (int)blist[ti.base + seg] : 0;
       const int prow = blk * seglen + (row & (seglen - 1));
       const bool ok = vseg && prow < rows_lv;
-      const int64_t goff = (int64_t)(ok ? prow : 0) * D;
+      const int rowel = (ok ? prow : 0) * D;
+      const uint32_t koff = (uint32_t)((rowel + 8 * (st_pchunk ^ k_swz<D>(row))) * (int)sizeof(T));
+      const uint32_t voff = (uint32_t)((rowel + 8 * (st_pchunk ^ v_swz<D>(row))) * (int)sizeof(T));
       if constexpr (kDirect) {
         const int blkoff = (wave * BPW + i) * 512;    // 1 KB block, in bf16 elements
-        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + goff + 8 * (st_pchunk ^ k_swz<D>(row))),
-                                         (lds_void*)(kbuf(P) + blkoff), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + goff + 8 * (st_pchunk ^ v_swz<D>(row))),
-                                         (lds_void*)(vbuf(P) + blkoff), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + koff), (lds_void*)(kbuf(P) + blkoff), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + voff), (lds_void*)(vbuf(P) + blkoff), 16, 0, 0);
       } else {
-        fk[i].load(reinterpret_cast<const float*>(kb + goff) + 8 * (st_pchunk ^ k_swz<D>(row)));
-        fv[i].load(reinterpret_cast<const float*>(vb + goff) + 8 * (st_pchunk ^ v_swz<D>(row)));
+        fk[i].load(reinterpret_cast<const float*>(kb + koff));
+        fv[i].load(reinterpret_cast<const float*>(vb + voff));
       }
       if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
     }
@@ -327,12 +331,21 @@ static hipError_t launch_attn_dtype(const AttnArgs& a, hipStream_t stream) {
   return a.q_block == 128 ? launch_attn_t<T, 64, 4>(a, stream) : launch_attn_t<T, 64, 2>(a, stream);
 }
 
+// Two attention kernels share the tile schedule and numerics: the single-group
+// kernel is the default (the faster one at the shapes measured); setting
+// PSA_ATTENTION_KERNEL=pp in the environment selects the two-group (ping-pong)
+// kernel. Read once per process.
+static int attention_kernel_choice() {
+  static const int choice = [] {
+    const char* e = std::getenv("PSA_ATTENTION_KERNEL");
+    return (e && std::strcmp(e, "pp") == 0) ? 1 : 0;
+  }();
+  return choice;
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
-#ifdef PSA_ATTN_TWO_GROUP
-  return launch_attention_pp(a, stream);
-#else
+  if (attention_kernel_choice() == 1) return launch_attention_pp(a, stream);
   return a.bf16 ? launch_attn_dtype<bf16_t>(a, stream) : launch_attn_dtype<float>(a, stream);
-#endif
 }
 
 }  // namespace psa
