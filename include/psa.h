@@ -64,7 +64,7 @@ typedef enum { PSA_F32 = 0, PSA_BF16 = 1 } psa_dtype_t;
 typedef enum { PSA_WS_ESTIMATE_MASK = 0, PSA_WS_ATTENTION_FWD = 1 } psa_workspace_kind_t;
 
 typedef struct {
-  int32_t B, H, H_kv, N, d;   /* d in {64, 128}; H % H_kv == 0                        */
+  int32_t B, H, H_kv, N, d;   /* d in {64, 128}; H % H_kv == 0; B * H <= 65535        */
   int32_t q_block;            /* query block size: 64 or 128                           */
   int32_t kv_block;           /* KV block size: 64                                     */
   int32_t num_levels;         /* L in [1, 4]: level l pools 2^l tokens                 */
@@ -111,7 +111,9 @@ psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const v
  * [0, n_dense_prefix) is set to level 0 for every query block.
  * thresholds: host array of num_levels floats, nondecreasing, each in [0, 1].
  * cmass_out (nullable): C as float32 [B, H, nqb, nkb].
- * workspace: psa_workspace_bytes(prob, PSA_WS_ESTIMATE_MASK) bytes of device memory.
+ * workspace: psa_workspace_bytes(prob, PSA_WS_ESTIMATE_MASK) bytes of device memory
+ * (mean queries, then block scores with rows padded to a power of two >= 64),
+ * 16-byte aligned; its contents on entry do not matter.
  * Supported: nkb <= 2048 (N <= 131072).
  */
 psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const float* k_bar,

@@ -57,6 +57,8 @@ psa_status_t check_problem(const psa_problem_t* p) {
     return fail(PSA_ERR_UNSUPPORTED, "tensor of %lld elements is too large", (long long)elems);
   if ((int64_t)p->B * p->H * ceil_div(p->N, p->q_block) >= ((int64_t)1 << 31) - 8)
     return fail(PSA_ERR_UNSUPPORTED, "too many query blocks");
+  if ((int64_t)p->B * p->H > 65535)   // one grid dimension spans batch x heads
+    return fail(PSA_ERR_UNSUPPORTED, "B * H = %lld exceeds 65535", (long long)p->B * p->H);
   return PSA_OK;
 }
 
@@ -82,8 +84,16 @@ float effective_scale(const psa_problem_t* p) {
   return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->d);
 }
 
-size_t mask_workspace(const psa_problem_t* p) {
+// Mask workspace: mean queries [B, H, nqb, d] then block scores [B, H, nqb, stride],
+// both float32 (the first part's size is a multiple of 256 bytes, so the second
+// stays 16-byte aligned).
+size_t mask_qbar_bytes(const psa_problem_t* p) {
   return (size_t)p->B * p->H * ceil_div(p->N, p->q_block) * p->d * sizeof(float);
+}
+size_t mask_workspace(const psa_problem_t* p) {
+  const int nkb = (int)ceil_div(p->N, psa::kKvBlock);
+  return mask_qbar_bytes(p) +
+         (size_t)p->B * p->H * ceil_div(p->N, p->q_block) * psa::mask_score_stride(nkb) * sizeof(float);
 }
 
 #define REQUIRE_PTR(ptr, name)                                                        \
@@ -171,6 +181,7 @@ psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const f
   psa::MaskArgs a{};
   a.q = q; a.k_bar = k_bar; a.level_map = level_map; a.cmass = cmass_out;
   a.qbar = static_cast<float*>(workspace);
+  a.z = reinterpret_cast<float*>(static_cast<char*>(workspace) + mask_qbar_bytes(prob));
   a.B = prob->B; a.H = prob->H; a.H_kv = prob->H_kv; a.N = prob->N; a.d = prob->d;
   a.q_block = prob->q_block;
   a.nqb = (int)ceil_div(prob->N, prob->q_block);

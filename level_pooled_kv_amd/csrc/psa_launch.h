@@ -20,7 +20,9 @@ struct PyramidArgs {
 };
 
 struct MaskArgs {
-  const void* q; const float* k_bar; int8_t* level_map; float* cmass; float* qbar;
+  const void* q; const float* k_bar; int8_t* level_map; float* cmass;
+  float* qbar;                   // workspace: [B, H, nqb, d] mean queries
+  float* z;                      // workspace: [B, H, nqb, mask_score_stride(nkb)] block scores
   int B, H, H_kv, N, d, q_block, nqb, nkb, L, n_dense_prefix;
   bool bf16;
   float scale;
@@ -40,6 +42,7 @@ struct AttnArgs {
 
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
+int mask_score_stride(int nkb);  // padded row length of the score workspace
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);      // picks a kernel
 hipError_t launch_attention_pp(const AttnArgs& a, hipStream_t stream);   // two-group kernel
 

@@ -41,7 +41,13 @@ def prob(psa, **kw):
 def test_sizes(psa):
     p = prob(psa)
     assert p.pyramid_rows == sum(math.ceil(32760 / 2 ** l) for l in (1, 2, 3))
-    assert p.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK) == 1 * 12 * 256 * 128 * 4
+    # mean queries [B,H,nqb,d] + block scores [B,H,nqb,512] (512 KV blocks, already a power of two)
+    assert p.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK) == 1 * 12 * 256 * 128 * 4 + 1 * 12 * 256 * 512 * 4
+    # score rows are padded to a power of two >= 64: 278 KV blocks -> 512, 32 -> 64
+    assert (prob(psa, H=48, H_kv=48, N=17776, d=64).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
+            == 48 * 139 * 64 * 4 + 48 * 139 * 512 * 4)
+    assert (prob(psa, H=2, H_kv=2, N=2048, d=64, q_block=64).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
+            == 2 * 32 * 64 * 4 + 2 * 32 * 64 * 4)
     assert p.workspace_bytes(psa.PSA_WS_ATTENTION_FWD) == 0
     assert prob(psa, num_levels=1).pyramid_rows == 0
     assert prob(psa, N=2045, num_levels=2).pyramid_rows == 1023
@@ -52,7 +58,7 @@ def test_sizes(psa):
     (dict(B=0), 1), (dict(N=-5), 1), (dict(H=12, H_kv=5), 1), (dict(num_levels=0), 1),
     (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
     (dict(d=96), 2), (dict(q_block=32), 2), (dict(kv_block=128), 2), (dict(num_levels=5), 2),
-    (dict(N=64 * 2048 + 1), 2),
+    (dict(N=64 * 2048 + 1), 2), (dict(B=2, H=40000, H_kv=40000, N=64), 2),
 ])
 def test_check_problem_rejects(psa, kw, status):
     p = prob(psa, **kw)
