@@ -71,41 +71,67 @@ qblock_mean_kernel(const T* __restrict__ q, float* __restrict__ qbar, int N, int
   }
 }
 
-// One 32 (KV blocks) x 32 (query blocks) tile of scores per wave. The contraction
-// index is split between the two lane halves as [0, D/2) and [D/2, D) (the same
-// split for both operands, so every product pairs matching elements).
+// One 32 (KV blocks) x 32 (query blocks) tile of scores per wave, kScoreWaves waves
+// (consecutive KV tiles) per workgroup sharing one query tile. Operand tiles are
+// staged through LDS with coalesced 16-byte loads (rows padded by 4 floats, so the
+// per-lane row reads of the MFMA operands are free of bank conflicts). The
+// contraction index is split between the two lane halves as [0, D/2) and
+// [D/2, D), the same split for both operands.
+constexpr int kScoreWaves = 2;
+
 template <int D>
-__global__ void __launch_bounds__(kMaskThreads)
+__global__ void __launch_bounds__(64 * kScoreWaves)
 block_score_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar, float* __restrict__ z,
                    int N, int H, int H_kv, int nqb, int nkb, int zstride, float scale) {
   constexpr int S = D / 2;                  // MFMA steps (k = 2 each)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kt = blockIdx.x * (kMaskThreads / 64) + wave;
-  if (kt * 32 >= nkb) return;               // whole wave; no barrier in this kernel
+  constexpr int RS = D + 4;                 // padded LDS row (floats)
+  constexpr int F4 = 32 * D / 4;            // float4 per 32-row tile
+  __shared__ __align__(16) float qs[32 * RS];
+  __shared__ __align__(16) float ks[kScoreWaves][32 * RS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int kt = blockIdx.x * kScoreWaves + wave;
+  const bool active = kt * 32 < nkb;        // whole wave
   const int qt = blockIdx.y;
   const int bh = blockIdx.z;
   const int b = bh / H, h = bh - b * H;
   const int g = h / (H / H_kv);
-  const int l32 = lane & 31, half = lane >> 5;
-  const int key = min(kt * 32 + l32, nkb - 1);
-  const int qi = min(qt * 32 + l32, nqb - 1);
-  const float4* ka = reinterpret_cast<const float4*>(kbar + ((int64_t)(b * H_kv + g) * nkb + key) * D + half * S);
-  const float4* qa = reinterpret_cast<const float4*>(qbar + ((int64_t)bh * nqb + qi) * D + half * S);
-  float4 kv[S / 4], qv[S / 4];
+
+  const float* qsrc = qbar + (int64_t)bh * nqb * D;
 #pragma unroll
-  for (int c = 0; c < S / 4; ++c) {
-    kv[c] = ka[c];
-    qv[c] = qa[c];
+  for (int c = 0; c < F4 / (64 * kScoreWaves); ++c) {
+    const int f = t + 64 * kScoreWaves * c;
+    const int row = f / (D / 4), col = 4 * (f % (D / 4));
+    const int qi = min(qt * 32 + row, nqb - 1);
+    *reinterpret_cast<float4*>(&qs[row * RS + col]) = *reinterpret_cast<const float4*>(qsrc + (int64_t)qi * D + col);
   }
+  if (active) {
+    const float* ksrc = kbar + (int64_t)(b * H_kv + g) * nkb * D;
+#pragma unroll
+    for (int c = 0; c < F4 / 64; ++c) {
+      const int f = lane + 64 * c;
+      const int row = f / (D / 4), col = 4 * (f % (D / 4));
+      const int key = min(kt * 32 + row, nkb - 1);
+      *reinterpret_cast<float4*>(&ks[wave][row * RS + col]) =
+          *reinterpret_cast<const float4*>(ksrc + (int64_t)key * D + col);
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+
+  const int l32 = lane & 31, half = lane >> 5;
+  const float* ka = &ks[wave][l32 * RS + half * S];
+  const float* qa = &qs[l32 * RS + half * S];
   f32x16 acc;
 #pragma unroll
   for (int x = 0; x < 16; ++x) acc[x] = 0.f;
 #pragma unroll
   for (int c = 0; c < S / 4; ++c) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[c].x, qv[c].x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[c].y, qv[c].y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[c].z, qv[c].z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[c].w, qv[c].w, acc, 0, 0, 0);
+    const float4 kv = *reinterpret_cast<const float4*>(ka + 4 * c);
+    const float4 qv = *reinterpret_cast<const float4*>(qa + 4 * c);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qv.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qv.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, qv.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, qv.w, acc, 0, 0, 0);
   }
   // accumulator v of lane l: query block 32 qt + l%32, KV block 32 kt + 8 (v/4) + 4 (l/32) + v%4
   const int row = qt * 32 + l32;
@@ -155,49 +181,146 @@ __device__ __forceinline__ float key_score(uint64_t k) {
   return __uint_as_float((key & 0x80000000u) ? key : (~key & 0x7fffffffu));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m);
+// Value of lane (lane ^ M), from VALU cross-lane ops only (no LDS round trip): DPP
+// quad permutes for 1 and 2, a half-row mirror (lane ^ 7) then a quad reverse (^ 3)
+// for 4, a row rotate by 8 for 8, and the gfx950 row swaps for 16 and 32 (with
+// a = b = x, permlane16_swap returns {x[l & ~16], x[l | 16]} per lane and
+// permlane32_swap {x[l & ~32], x[l | 32]}).
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
+  else if constexpr (M == 4) {
+    const int m7 = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(m7, 0x1B, 0xF, 0xF, true);
+  } else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, true);
+  else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    static_assert(M == 32, "lane distance");
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? p[0] : p[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t x, int lane) {
+  const uint32_t lo = xor_lane<M>((uint32_t)x, lane);
+  const uint32_t hi = xor_lane<M>((uint32_t)(x >> 32), lane);
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Bitonic sort, ascending, of the 64 E keys of one wave; element e = E * lane + r is
-// key[r] of lane `lane`. Pairs at distance < E are in one lane; at distance >= E the
-// partner is lane ^ (distance / E), same r.
-template <int E>
+// Ascending bitonic sort of the 64 E keys of one wave; element e = E * lane + r is
+// key[r] of lane `lane`. Pairs at distance J < E are in one lane; at J >= E the
+// partner is lane ^ (J / E), same r. Every exchange is a select on a compare, no
+// branch; the network is unrolled at compile time, so every direction test folds to
+// a per-lane constant.
+template <int E, int M>
+__device__ __forceinline__ void stage_cross64(uint64_t (&key)[E], int lane, int k) {
+  const bool upper = (lane & M) != 0;                   // holds the higher element of its pair
+  const bool asc = ((E * lane) & k) == 0;               // k >= 2E: the same for every r
+  const bool keep_max = upper == asc;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const uint64_t y = xor_lane64<M>(key[r], lane);
+    key[r] = ((y > key[r]) == keep_max) ? y : key[r];
+  }
+}
+template <int E, int J>
+__device__ __forceinline__ void stage_in64(uint64_t (&key)[E], int lane, int k) {
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    if (r & J) continue;
+    const bool asc = ((E * lane + r) & k) == 0;
+    const uint64_t a = key[r], c = key[r + J];
+    const bool swap = (a > c) == asc;
+    key[r] = swap ? c : a;
+    key[r + J] = swap ? a : c;
+  }
+}
+template <int E, int K, int J>
+__device__ __forceinline__ void merge64(uint64_t (&key)[E], int lane) {
+  if constexpr (J > 0) {
+    if constexpr (J >= E) stage_cross64<E, J / E>(key, lane, K);
+    else stage_in64<E, J>(key, lane, K);
+    merge64<E, K, J / 2>(key, lane);
+  }
+}
+template <int E, int K = 2>
 __device__ __forceinline__ void wave_bitonic_sort(uint64_t (&key)[E], int lane) {
-  constexpr int NP = 64 * E;
-#pragma unroll
-  for (int k = 2; k <= NP; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= E) {
-        const int m = j / E;
-        const bool upper = (lane & m) != 0;                 // holds the higher element of its pair
-        const bool asc = ((E * lane) & k) == 0;             // k >= 2E: the same for every r
-        const bool keep_max = upper == asc;
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const uint64_t y = shfl_xor_u64(key[r], m);
-          const uint64_t x = key[r];
-          const bool take = keep_max ? (y > x) : (y < x);
-          key[r] = take ? y : x;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          if (r & j) continue;
-          const bool asc = ((E * lane + r) & k) == 0;
-          const uint64_t a = key[r], c = key[r + j];
-          const bool swap = (a > c) == asc;
-          key[r] = swap ? c : a;
-          key[r + j] = swap ? a : c;
-        }
-      }
-    }
+  if constexpr (K <= 64 * E) {
+    merge64<E, K, K / 2>(key, lane);
+    wave_bitonic_sort<E, 2 * K>(key, lane);
   }
 }
 
+// 32-bit keys: the order word alone (no index). Exchanges are v_med3_u32 against 0
+// (minimum) or ~0 (maximum), one VALU op per element of a cross-lane stage.
+__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
+  return min(max(a, b), max(min(a, b), c));
+}
+__device__ __forceinline__ uint32_t score_key(float z) {
+  const uint32_t u = __float_as_uint(z + 0.0f);
+  return (u & 0x80000000u) ? u : (~u & 0x7fffffffu);
+}
+__device__ __forceinline__ float key32_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? key : (~key & 0x7fffffffu));
+}
+constexpr uint32_t kPadKey32 = 0xFFFFFFFFu;   // above every finite score's key
+
+template <int E, int M>
+__device__ __forceinline__ void stage_cross32(uint32_t (&key)[E], int lane, int k) {
+  const bool upper = (lane & M) != 0;
+  const bool asc = ((E * lane) & k) == 0;
+  const uint32_t c = (upper == asc) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int r = 0; r < E; ++r) key[r] = med3u(key[r], xor_lane<M>(key[r], lane), c);
+}
+template <int E, int J>
+__device__ __forceinline__ void stage_in32(uint32_t (&key)[E], int lane, int k) {
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    if (r & J) continue;
+    const uint32_t clo = ((E * lane + r) & k) == 0 ? 0u : 0xFFFFFFFFu;
+    const uint32_t a = key[r], b = key[r + J];
+    key[r] = med3u(a, b, clo);
+    key[r + J] = med3u(a, b, ~clo);
+  }
+}
+template <int E, int K, int J>
+__device__ __forceinline__ void merge32(uint32_t (&key)[E], int lane) {
+  if constexpr (J > 0) {
+    if constexpr (J >= E) stage_cross32<E, J / E>(key, lane, K);
+    else stage_in32<E, J>(key, lane, K);
+    merge32<E, K, J / 2>(key, lane);
+  }
+}
+template <int E, int K = 2>
+__device__ __forceinline__ void wave_bitonic_sort32(uint32_t (&key)[E], int lane) {
+  if constexpr (K <= 64 * E) {
+    merge32<E, K, K / 2>(key, lane);
+    wave_bitonic_sort32<E, 2 * K>(key, lane);
+  }
+}
+
+// Exclusive prefix, across the wave, of per-lane totals.
+__device__ __forceinline__ float wave_exclusive_sum(float tot, int lane) {
+  float incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  return incl - tot;
+}
+
+// One wave per query-block row. Fast path: sort the 32-bit score keys; with no two
+// equal scores the mass ranked ahead of a block is a prefix of the sorted masses, so
+// level l takes exactly the blocks whose key is at most the key at the last sorted
+// position with prefix mass below tau_l. Rows with equal scores (ties are broken by
+// block index) and calls that want the cumulative mass itself take the exact path:
+// a sort of 64-bit (score, index) keys. Both paths sum the same masses in the same
+// order, so they give the same levels.
 template <int E>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
@@ -227,40 +350,87 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     if (E * lane + r < nkb) mx = fmaxf(mx, zz[r]);
   mx = wave_max(mx);
   float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    if (E * lane + r < nkb) s += __expf(zz[r] - mx);
+  s = wave_sum(s);
+  const float inv_s = 1.0f / s;
+  const float tau[4] = {tau0, tau1, tau2, tau3};
+  int8_t* lrow = level_map + (int64_t)row * nkb;
+
+  if (cmass == nullptr) {
+    uint32_t orig[E], key[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      orig[r] = E * lane + r < nkb ? score_key(zz[r]) : kPadKey32;
+      key[r] = orig[r];
+    }
+    wave_bitonic_sort32<E>(key, lane);
+    bool tie = false;
+#pragma unroll
+    for (int r = 0; r + 1 < E; ++r) tie |= key[r] == key[r + 1] && key[r] != kPadKey32;
+    const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
+    tie |= lane < 63 && key[E - 1] == next_first && key[E - 1] != kPadKey32;
+    if (__ballot(tie) == 0) {
+      float p[E], tot = 0.f;
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        p[r] = key[r] != kPadKey32 ? __expf(key32_score(key[r]) - mx) * inv_s : 0.f;
+        tot += p[r];
+      }
+      float run = wave_exclusive_sum(tot, lane);
+      int cnt[kMaxLevels] = {0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const float C = run;
+        run += p[r];
+        const bool real = key[r] != kPadKey32;
+#pragma unroll
+        for (int l = 0; l < kMaxLevels; ++l) cnt[l] += (int)__popcll(__ballot(real && C < tau[l]));
+      }
+      // key at sorted position cnt[l] - 1: the last block level l (or a lower one) takes
+      uint32_t cut[kMaxLevels];
+#pragma unroll
+      for (int l = 0; l < kMaxLevels; ++l) {
+        const int pos = cnt[l] - 1;
+        uint32_t v = key[0];
+#pragma unroll
+        for (int r = 1; r < E; ++r)
+          if (pos >= 0 && pos % E == r) v = key[r];
+        cut[l] = pos >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v, pos / E) : 0u;
+      }
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const int j = E * lane + r;
+        if (j < nkb) {
+          int lev = -1;
+#pragma unroll
+          for (int l = kMaxLevels - 1; l >= 0; --l)
+            if (l < L && cnt[l] > 0 && orig[r] <= cut[l]) lev = l;
+          if (64 * j < n_dense_prefix) lev = 0;
+          lrow[j] = (int8_t)lev;
+        }
+      }
+      return;
+    }
+  }
+
+  // ---- exact path: sort (score, index) keys
   uint64_t key[E];
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const int j = E * lane + r;
-    if (j < nkb) {
-      s += expf(zz[r] - mx);
-      key[r] = rank_key(zz[r], j);
-    } else {
-      key[r] = ~0ull;                        // padding sorts last
-    }
+    key[r] = j < nkb ? rank_key(zz[r], j) : ~0ull;   // padding sorts last
   }
-  s = wave_sum(s);
-  const float inv_s = 1.0f / s;
-
   wave_bitonic_sort<E>(key, lane);
-
-  // ---- exclusive prefix of the masses in rank order: lane-local, then across lanes
   float p[E], tot = 0.f;
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const uint32_t j = (uint32_t)key[r];
-    p[r] = j < (uint32_t)nkb ? expf(key_score(key[r]) - mx) * inv_s : 0.f;
+    p[r] = j < (uint32_t)nkb ? __expf(key_score(key[r]) - mx) * inv_s : 0.f;
     tot += p[r];
   }
-  float incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  float run = incl - tot;
-
-  const float tau[4] = {tau0, tau1, tau2, tau3};
-  int8_t* lrow = level_map + (int64_t)row * nkb;
+  float run = wave_exclusive_sum(tot, lane);
   float* crow = cmass ? cmass + (int64_t)row * nkb : nullptr;
 #pragma unroll
   for (int r = 0; r < E; ++r) {
@@ -301,8 +471,8 @@ static hipError_t launch_mask_t(const MaskArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int zstride = mask_score_stride(a.nkb);
   const int ktiles = (a.nkb + 31) / 32;
-  dim3 sgrid((ktiles + 3) / 4, (a.nqb + 31) / 32, a.B * a.H);
-  hipLaunchKernelGGL((block_score_kernel<D>), sgrid, dim3(kMaskThreads), 0, stream, a.qbar, a.k_bar, a.z, a.N,
+  dim3 sgrid((ktiles + kScoreWaves - 1) / kScoreWaves, (a.nqb + 31) / 32, a.B * a.H);
+  hipLaunchKernelGGL((block_score_kernel<D>), sgrid, dim3(64 * kScoreWaves), 0, stream, a.qbar, a.k_bar, a.z, a.N,
                      a.H, a.H_kv, a.nqb, a.nkb, zstride, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

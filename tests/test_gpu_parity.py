@@ -59,8 +59,11 @@ def run_small(psa, label, q, k, v, *, H, H_kv, d, q_block, L, dtype, tau, n_dens
 
     # step 2
     lev, cm = psa.psa_estimate_mask(prob, qd, kbar, tau, n_dense_prefix, want_cmass=True)
+    lev_fast, _ = psa.psa_estimate_mask(prob, qd, kbar, tau, n_dense_prefix)
     torch.cuda.synchronize()
     lev_gpu = lev.cpu().numpy()
+    # without the cumulative-mass output the kernel may take its 32-bit-key path: same levels
+    assert np.array_equal(lev_fast.cpu().numpy(), lev_gpu), label
     nacc = check_mask(lev_gpu, ora["mask"], tau, L, n_dense_prefix, label=label)
     check_cmass(to_host(cm), ora["mask"], label)
 
@@ -167,6 +170,26 @@ def test_identical_key_block_level_invariant(psa):
         assert np.abs(outs[l] - outs[0]).max() < 2e-2
 
 
+def test_mask_equal_scores(psa):
+    # KV blocks 1..6 hold the same keys, so every query block sees equal scores for
+    # them; the order among equal scores is by block index (exact path of the kernel)
+    q, k, v = random_qkv(10, 1, 2, 2, 1024, 64, "bf16")
+    k[:, :, 128:448] = np.tile(k[:, :, 64:128], (1, 1, 5, 1))
+    tau = (0.1, 0.3, 0.5, 0.7)
+    ora = o.run_forward(q, k, v, 64, 64, tau, 4, 1 / math.sqrt(64), "bf16", 0)
+    z = ora["mask"]["z"]
+    assert np.all(z[..., 1:7] == z[..., 1:2])
+    prob = psa.Problem(B=1, H=2, H_kv=2, N=1024, d=64, q_block=64, num_levels=4, dtype="bf16")
+    say("mask with equal scores (blocks 1..6)")
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    _, _, kbar = psa.psa_build_pyramid(prob, kd, to_device(v, "bf16"))
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, tau)
+    lev_c, _ = psa.psa_estimate_mask(prob, qd, kbar, tau, want_cmass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lev, lev_c)
+    check_mask(lev.cpu().numpy(), ora["mask"], tau, 4, 0, label="equal scores")
+
+
 def test_deterministic(psa):
     q, k, v = random_qkv(9, 1, 2, 2, 3000, 128, "bf16")
     prob = psa.Problem(B=1, H=2, H_kv=2, N=3000, d=128, q_block=128, num_levels=4, dtype="bf16")
@@ -194,7 +217,9 @@ def full_workload(psa, name, n_items=8, seed=0):
     say(f"{name}: GPU pyramid + mask")
     kp, vp, kbar = psa.psa_build_pyramid(prob, kd, vd)
     lev, cm = psa.psa_estimate_mask(prob, qd, kbar, tau, w.n_dense_prefix, want_cmass=True)
+    lev_fast, _ = psa.psa_estimate_mask(prob, qd, kbar, tau, w.n_dense_prefix)
     torch.cuda.synchronize()
+    assert torch.equal(lev_fast, lev), name
 
     say(f"{name}: oracle pyramid per KV head")
     kbar_g = to_host(kbar)
