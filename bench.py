@@ -10,7 +10,7 @@ the roofline's kernel).
 
 Throughput is effective TFLOP/s: FLOPs of QK^T and PV on the retained pooled rows
 only (sum over retained blocks of 4 * rows * pooled_rows * d), divided by the step
-time. The CPU baseline times the float64 oracle on four heads of the same workload.
+time. The CPU baseline times the float64 oracle on ten heads of the same workload.
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -32,7 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan13b_traffic.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "level_pooled_kv_amd", "csrc", f)
-                for f in ("psa_attn_common.h", "psa_attention.hip", "psa_attention_pp.hip")]
+                for f in ("psa_attn_common.h", "psa_attention.hip")]
 
 
 def attention_source_hash() -> str:
@@ -44,8 +44,6 @@ def attention_source_hash() -> str:
 
 def attention_kernel_name(d: int, q_block: int, dtype: str) -> str:
     t = "bf16" if dtype == "bf16" else "float"
-    if os.environ.get("PSA_ATTENTION_KERNEL") == "pp":
-        return f"pyramid_attn_fwd_pp_kernel<{t},{d},{q_block // 32}>"
     return f"pyramid_attn_fwd_kernel<{t},{d},{q_block // 32}>"
 
 
@@ -86,12 +84,12 @@ def traffic_from_profile():
 
 
 def cpu_baseline(w, q, k, v, tau):
-    """Oracle (float64 NumPy) on a bounded sample: every step for query heads 0..3 (and their KV heads)."""
+    """Oracle (float64 NumPy) on a bounded sample: every step for query heads 0..9 (and their KV heads)."""
     from threadpoolctl import threadpool_info
     from oracle import psa_oracle as o
 
     t0 = time.perf_counter()
-    nh = min(4, w.H)
+    nh = min(10, w.H)
     qh = q[:, :nh].astype(np.float64)
     kh = k[:, :nh].astype(np.float64)
     vh = v[:, :nh].astype(np.float64)
@@ -212,7 +210,7 @@ def main():
         "levels": level_histogram(lm),
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on one head", file=sys.stderr, flush=True)
+        print("[bench] timing the oracle on a head sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, tau)
     else:
         result["cpu_baseline"] = None

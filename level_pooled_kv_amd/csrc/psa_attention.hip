@@ -36,8 +36,6 @@
 //    grows by more than 2^8, which keeps every P <= 256 and skips most rescales.
 #include "psa_attn_common.h"
 
-#include <cstdlib>
-#include <cstring>
 
 #include <type_traits>
 
@@ -331,20 +329,7 @@ static hipError_t launch_attn_dtype(const AttnArgs& a, hipStream_t stream) {
   return a.q_block == 128 ? launch_attn_t<T, 64, 4>(a, stream) : launch_attn_t<T, 64, 2>(a, stream);
 }
 
-// Two attention kernels share the tile schedule and numerics: the single-group
-// kernel is the default (the faster one at the shapes measured); setting
-// PSA_ATTENTION_KERNEL=pp in the environment selects the two-group (ping-pong)
-// kernel. Read once per process.
-static int attention_kernel_choice() {
-  static const int choice = [] {
-    const char* e = std::getenv("PSA_ATTENTION_KERNEL");
-    return (e && std::strcmp(e, "pp") == 0) ? 1 : 0;
-  }();
-  return choice;
-}
-
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
-  if (attention_kernel_choice() == 1) return launch_attention_pp(a, stream);
   return a.bf16 ? launch_attn_dtype<bf16_t>(a, stream) : launch_attn_dtype<float>(a, stream);
 }
 

@@ -56,43 +56,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // their maxima).
 __host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
 
-// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane i copies
-// global [sbase + voff_i, +16) to LDS [lds_base + 16 i, +16). lds_base and sbase must be
-// wave-uniform (they are made so with readfirstlane). Written as inline asm so that the
-// compiler's wait-count tracking does not see these loads at all: its tracking of which
-// LDS buffer a direct load targets does not survive the loops here and would make every
-// LDS read wait for every prefetch. Callers retire the loads explicitly (wait_vmcnt)
-// before the barrier that publishes them. No register outputs; M0 is set here and is not
-// otherwise used by these kernels.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds_base) {
-  const uint32_t m0v =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base);
-  // readfirstlane returns a signed int: each half goes through uint32_t before widening,
-  // or a low half at or above 2^31 would be sign-extended over the high half.
-  const uint64_t b = (uint64_t)(uintptr_t)sbase;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff), "s"(bu) : "memory", "m0");
-#pragma clang diagnostic pop
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight. Written as
-// inline asm on purpose: the compiler tracks which LDS buffers in-flight direct loads
-// target and only waits where a read may alias one; an s_waitcnt it can see (the
-// builtin) makes it lose that tracking and wait for every load before any LDS read.
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier that retires this wave's LDS operations (lgkmcnt(0)) but not its
-// in-flight direct global->LDS loads: unlike __syncthreads(), whose release fence drains
-// every outstanding LDS write including those loads, it lets a prefetch stay in flight
-// across the barrier. A wave retires the direct loads it must publish with an explicit
-// s_waitcnt vmcnt before calling it. The asm statement is also a compiler memory barrier.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Per-tile descriptor (built once per query block): level | first block-list index << 2 |
 // valid segments << 16 | irregular << 31.

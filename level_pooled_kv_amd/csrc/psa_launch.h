@@ -43,7 +43,6 @@ struct AttnArgs {
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
 int mask_score_stride(int nkb);  // padded row length of the score workspace
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);      // picks a kernel
-hipError_t launch_attention_pp(const AttnArgs& a, hipStream_t stream);   // two-group kernel
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace psa
