@@ -84,15 +84,17 @@ def traffic_from_profile():
 
 
 def cpu_baseline(w, q, k, v, tau):
-    """Oracle (float64 NumPy) on a bounded sample: every step for query heads 0..9 (and their KV heads)."""
+    """Oracle (float64 NumPy) on a bounded sample: every step for about ten query heads (whole KV-head groups)."""
     from threadpoolctl import threadpool_info
     from oracle import psa_oracle as o
 
     t0 = time.perf_counter()
-    nh = min(10, w.H)
+    group = w.H // w.H_kv                       # query heads per KV head
+    nkv = max(1, min(w.H_kv, 10 // group))      # whole groups, about ten query heads
+    nh = nkv * group
     qh = q[:, :nh].astype(np.float64)
-    kh = k[:, :nh].astype(np.float64)
-    vh = v[:, :nh].astype(np.float64)
+    kh = k[:, :nkv].astype(np.float64)
+    vh = v[:, :nkv].astype(np.float64)
     res = o.run_forward(qh, kh, vh, w.q_block, w.kv_block, tau, w.num_levels, w.scale, w.dtype,
                         w.n_dense_prefix)
     dt = time.perf_counter() - t0
