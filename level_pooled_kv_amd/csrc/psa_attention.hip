@@ -151,6 +151,42 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
     }
   };
+  // Direct-load path: the byte offsets of tile t's staged rows are computed up front
+  // (with the tile's logit corrections when irregular), and the loads themselves are
+  // issued one at a time between the MFMAs of the current tile, so no wave stalls
+  // behind a burst of loads queued at the CU's load path.
+  struct Stage { const char* kb; const char* vb; uint32_t koff[BPW], voff[BPW]; };
+  auto stage_addr = [&](int t, auto P) {
+    constexpr int buf = P();
+    Stage st;
+    const TileInfo ti = tile_info(t);
+    const int lvl = ti.lvl;
+    const int sh = 6 - lvl, seglen = 64 >> lvl;
+    const int rows_lv = level_rows(lvl);
+    const int64_t loff = (int64_t)level_off(lvl) * D;
+    st.kb = reinterpret_cast<const char*>(lvl == 0 ? kh : kph + loff);
+    st.vb = reinterpret_cast<const char*>(lvl == 0 ? vh : vph + loff);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int row = st_row0 + RPB * i;
+      const int seg = row >> sh;
+      const bool vseg = seg < ti.nseg;
+      const int blk = vseg ? (int)blist[ti.base + seg] : 0;
+      const int prow = blk * seglen + (row & (seglen - 1));
+      const bool ok = vseg && prow < rows_lv;
+      const int rowel = (ok ? prow : 0) * D;
+      st.koff[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ k_swz<D>(row))) * (int)sizeof(T));
+      st.voff[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ v_swz<D>(row))) * (int)sizeof(T));
+      if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
+    }
+    return st;
+  };
+  auto dma_k = [&](const Stage& st, int i, auto P) {
+    __builtin_amdgcn_global_load_lds((gbl_void*)(st.kb + st.koff[i]), (lds_void*)(kbuf(P) + (wave * BPW + i) * 512), 16, 0, 0);
+  };
+  auto dma_v = [&](const Stage& st, int i, auto P) {
+    __builtin_amdgcn_global_load_lds((gbl_void*)(st.vb + st.voff[i]), (lds_void*)(vbuf(P) + (wave * BPW + i) * 512), 16, 0, 0);
+  };
   auto commit_tile = [&](auto P) {
     if constexpr (!kDirect) {
 #pragma unroll
@@ -188,7 +224,12 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   auto body = [&](int t, auto P) {
     constexpr int buf = P();
     using PN = std::integral_constant<int, 1 - P()>;
-    if (t + 1 < T_total) issue_tile(t + 1, PN{});
+    // the next tile's staging (past the last tile: a reload of the last tile into the
+    // idle buffers, so the interleaved loads need no branch)
+    Stage st{};
+    if constexpr (kDirect) st = stage_addr(min(t + 1, T_total - 1), PN{});
+    else if (t + 1 < T_total) issue_tile(t + 1, PN{});
+    constexpr int SK = 2 * C::kQc / BPW, SV = 4 * C::kDt / BPW;   // MFMAs per interleaved load
     const TileInfo ti = tile_info(t);
     const int lvl = ti.lvl;
     const bool irr = ti.irr;
@@ -208,6 +249,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       for (int c = 0; c < C::kQc; ++c) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr_l + (((2 * c + half) ^ swz) * 8));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sacc[kb], 0, 0, 0);
+        if constexpr (kDirect) {
+          const int j = kb * C::kQc + c;
+          if ((j + 1) % SK == 0) dma_k(st, j / SK, PN{});
+        }
       }
     }
     if (irr) {
@@ -271,6 +316,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         }
         const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, preg[c], oacc[tt], 0, 0, 0);
+        if constexpr (kDirect) {
+          const int j = tt * 4 + c;
+          if ((j + 1) % SV == 0) dma_v(st, j / SV, PN{});
+        }
       }
     }
 
