@@ -14,10 +14,13 @@ method as the pages describe it:
   pooling, each level coarser) and the paragraph naming the three components
   (progressive pooling, a multi-level mask generator driven by query-block /
   KV-block importance, attention that keeps the probability distribution
-  consistent); ablation paragraph (threshold-based assignment).
+  consistent); ablation paragraph (threshold-based assignment preferred to
+  quantile-based; multi-level masks preferred to binary ones).
 * skillmd.com "Psa Pyramid Sparse Attention", sections "Pooled KV cache
-  creation" (pool factor 2**level, average pooling over tokens) and "Block
-  importance scoring" (query against the block's mean key).
+  creation" (pool factor 2**level, average pooling over tokens), "Block
+  importance scoring" (query against the block's mean key) and "Level
+  assignment" (fixed shares of the score-ranked blocks per level: the ranked
+  rule that the top168.com ablation compares with thresholds).
 
 Where the pages leave a step open, the reading taken is stated in the
 function's docstring. The precise arithmetic of the probability-consistency
@@ -234,6 +237,62 @@ def estimate_mask(q: np.ndarray, k: np.ndarray, q_block: int, kv_block: int,
     C = cumulative_mass(z, p)
     lev = assign_levels(C, thresholds, num_levels, n_dense_prefix, kv_block)
     return {"qbar": qbar, "kbar": kbar, "z": z, "p": p, "cmass": C, "levels": lev}
+
+
+# ----------------------------------------------------------------------------
+# O4b: ranked (quantile) level assignment, the ablation's alternative rule
+# ----------------------------------------------------------------------------
+
+def rank_counts(fractions: Sequence[float], num_levels: int, nkb: int) -> List[int]:
+    """Cumulative block counts K_l = floor(f_l * nkb), the product taken in float64.
+
+    skillmd.com "Level assignment" keeps int(num_blocks * keep_ratio) blocks at full
+    resolution; a fraction per level generalises that keep ratio to every level."""
+    return [int(math.floor(float(f) * nkb)) for f in list(fractions)[:num_levels]]
+
+
+def block_ranks(z: np.ndarray) -> np.ndarray:
+    """rank[..., j] = position of block j in importance order (0 = most important)."""
+    R = np.empty(z.shape, dtype=np.int64)
+    flat_z = z.reshape(-1, z.shape[-1])
+    flat_R = R.reshape(-1, z.shape[-1])
+    for r in range(flat_z.shape[0]):
+        flat_R[r, importance_order(flat_z[r])] = np.arange(z.shape[-1])
+    return R
+
+
+def assign_levels_ranked(z: np.ndarray, fractions: Sequence[float], num_levels: int,
+                         n_dense_prefix: int = 0, kv_block: int = 64) -> np.ndarray:
+    """level_j = min{l : rank_j < K_l}, or -1 (pruned) if no level qualifies; then the
+    KV blocks overlapping tokens [0, n_dense_prefix) are set to level 0.
+
+    The pages rank blocks by score and give fixed shares of them to each level
+    (skillmd.com "Level assignment"; the top168.com ablation calls this the
+    quantile-based rule). Reading: the blocks left after the keep ratio are taken
+    in importance order, so a less important block never gets a finer level."""
+    K = rank_counts(fractions, num_levels, z.shape[-1])
+    rank = block_ranks(z)
+    lev = np.full(z.shape, -1, dtype=np.int8)
+    for l in range(num_levels - 1, -1, -1):
+        lev[rank < K[l]] = l
+    if n_dense_prefix > 0:
+        nforce = -(-n_dense_prefix // kv_block)
+        lev[..., :nforce] = 0
+    return lev
+
+
+def estimate_mask_ranked(q: np.ndarray, k: np.ndarray, q_block: int, kv_block: int,
+                         fractions: Sequence[float], num_levels: int, scale: float,
+                         n_dense_prefix: int = 0) -> Dict[str, np.ndarray]:
+    """The mask step with the ranked rule; scores, p and C as in estimate_mask."""
+    N = q.shape[-2]
+    qbar = block_means(q, q_block)
+    kbar = block_means(k, kv_block)
+    z = block_scores(qbar, kbar, block_sizes(N, kv_block), scale)
+    p = softmax_rows(z)
+    C = cumulative_mass(z, p)
+    lev = assign_levels_ranked(z, fractions, num_levels, n_dense_prefix, kv_block)
+    return {"qbar": qbar, "kbar": kbar, "z": z, "p": p, "cmass": C, "rank": block_ranks(z), "levels": lev}
 
 
 # ----------------------------------------------------------------------------

@@ -219,6 +219,108 @@ def test_dense_prefix_forced_after_ranking():
     np.testing.assert_array_equal(forced["cmass"], plain["cmass"])
 
 
+# ----------------------------------------------------------------------------- ranked rule (O4b)
+
+def brute_rank(z_row, j):
+    return sum(1 for k in range(len(z_row)) if z_row[k] > z_row[j] or (z_row[k] == z_row[j] and k < j))
+
+
+def test_rank_counts_follow_the_keep_ratio_expression():
+    # skillmd.com "Level assignment" keeps int(num_blocks * keep_ratio) blocks
+    for nkb, f in [(10, 0.7), (100, 0.29), (30, 0.1), (512, 0.1), (278, 0.4), (7, 1.0), (7, 0.0)]:
+        assert o.rank_counts([f], 1, nkb) == [int(nkb * f)]
+    assert o.rank_counts([0.1, 0.4, 0.7, 1.0], 2, 30) == [3, 12]
+
+
+def test_ranked_levels_brute_force_with_ties():
+    z = np.round(rng(40).standard_normal((5, 37)), 1)       # many exact ties
+    fr = (0.05, 0.3, 0.3, 0.8)                                # level 2 empty
+    lev = o.assign_levels_ranked(z, fr, 4)
+    K = [int(37 * f) for f in fr]
+    for r in range(5):
+        for j in range(37):
+            rk = brute_rank(z[r], j)
+            ok = [l for l in range(4) if rk < K[l]]
+            assert lev[r, j] == (min(ok) if ok else -1)
+    assert not np.any(lev == 2)
+    for l, n in enumerate(np.diff([0] + K)):
+        assert np.all((lev == l).sum(axis=1) == n)
+
+
+def test_ranked_keep_ratio_split_into_thirds():
+    # The page's rule: the top int(n * 0.1) blocks at level 0, the rest split into
+    # thirds for levels 1..3 (taken in score order, the reading stated in the oracle).
+    n = 30
+    z = rng(41).standard_normal((1, n))
+    order = np.argsort(-z[0], kind="stable")
+    keep = order[:int(n * 0.1)]
+    rest = order[int(n * 0.1):]
+    expect = np.empty(n, dtype=int)
+    expect[keep] = 0
+    expect[rest[:len(rest) // 3]] = 1
+    expect[rest[len(rest) // 3:2 * len(rest) // 3]] = 2
+    expect[rest[2 * len(rest) // 3:]] = 3
+    lev = o.assign_levels_ranked(z, (0.1, 0.4, 0.7, 1.0), 4)
+    np.testing.assert_array_equal(lev[0], expect)
+
+
+def test_ranked_binary_top_k_is_stable_argsort_prefix():
+    z = rng(42).standard_normal((4, 3, 50))
+    z[..., 7] = z[..., 11]
+    for k in (0, 1, 13, 50):
+        lev = o.assign_levels_ranked(z, [k / 50], 1)
+        for idx in np.ndindex(4, 3):
+            top = np.sort(np.argsort(-z[idx], kind="stable")[:k])
+            np.testing.assert_array_equal(np.flatnonzero(lev[idx] == 0), top)
+            assert np.all(lev[idx][lev[idx] != 0] == -1)
+    zt = torch.from_numpy(rng(43).standard_normal((6, 40)))
+    lev = o.assign_levels_ranked(zt.numpy(), [10 / 40], 1)
+    for r in range(6):
+        ti = np.sort(torch.topk(zt[r], 10).indices.numpy())
+        np.testing.assert_array_equal(np.flatnonzero(lev[r] == 0), ti)
+
+
+def test_ranked_uniform_scores_closed_form():
+    # Q = 0: every score is ln 64, ranks follow the block index
+    N, nkb = 2048, 32
+    q = np.zeros((1, 1, N, 4))
+    k = rng(44).standard_normal((1, 1, N, 4))
+    fr = (0.125, 0.5, 0.5, 0.75)
+    m = o.estimate_mask_ranked(q, k, 64, 64, fr, 4, 0.5)
+    j = np.arange(nkb)
+    K = [4, 16, 16, 24]
+    expect = np.array([min([l for l in range(4) if jj < K[l]], default=-1) for jj in j])
+    np.testing.assert_array_equal(m["levels"][0, 0, 0], expect)
+    np.testing.assert_array_equal(m["rank"][0, 0, 0], j)
+
+
+def test_ranked_equals_threshold_rule_at_equal_counts():
+    # Both rules give each level a prefix of the same importance order, so with the
+    # per-level counts the thresholds select, the ranked rule gives the same map.
+    q = rng(45).standard_normal((1, 1, 128, 8))
+    k = rng(46).standard_normal((1, 1, 2048, 8))
+    q = np.concatenate([q] * 16, axis=2)
+    tau = (0.3, 0.5, 0.7, 0.9)
+    thr = o.estimate_mask(q, k, 2048, 64, tau, 4, 0.9)
+    assert thr["levels"].shape == (1, 1, 1, 32)
+    C = thr["cmass"][0, 0, 0]
+    fr = [float(np.sum(C < np.float32(t))) / 32 for t in tau]
+    ranked = o.estimate_mask_ranked(q, k, 2048, 64, fr, 4, 0.9)
+    assert len(set(fr)) == 4
+    np.testing.assert_array_equal(ranked["levels"], thr["levels"])
+
+
+def test_ranked_dense_prefix_forced_after_ranking():
+    q = rng(47).standard_normal((1, 2, 640, 8))
+    k = rng(48).standard_normal((1, 2, 640, 8))
+    fr = (0.2, 0.4, 0.6, 0.8)
+    plain = o.estimate_mask_ranked(q, k, 128, 64, fr, 4, 0.35)
+    forced = o.estimate_mask_ranked(q, k, 128, 64, fr, 4, 0.35, n_dense_prefix=129)
+    assert np.all(forced["levels"][..., :3] == 0)
+    np.testing.assert_array_equal(forced["levels"][..., 3:], plain["levels"][..., 3:])
+    np.testing.assert_array_equal(forced["rank"], plain["rank"])
+
+
 # ----------------------------------------------------------------------------- attention (O6)
 
 def brute_attention_row(qr, keys, vals, weights_log, scale):
