@@ -1,9 +1,12 @@
 """Benchmark of the MI355X Pyramid Sparse Attention forward path (one GPU).
 
     python bench.py [--steps K] [--warmup W] [--workload wan13b] [--no-cpu-baseline]
+                    [--rule threshold|ranked] [--fractions f0,f1,f2,f3]
+    python bench.py --compare-rules [--workload wan13b]   (accuracy of the mask rules)
 
 A step is one pass of the whole forward path over one batch of resident inputs:
-psa_build_pyramid, psa_estimate_mask and psa_attention_fwd, enqueued on one stream.
+psa_build_pyramid, psa_estimate_mask (psa_estimate_mask_ranked with --rule ranked) and
+psa_attention_fwd, enqueued on one stream.
 W untimed steps, then K timed steps bracketed by device synchronisation; HIP events
 around every call give per-call times (the attention call is a single kernel launch,
 the roofline's kernel).
@@ -83,7 +86,7 @@ def traffic_from_profile():
         return None
 
 
-def cpu_baseline(w, q, k, v, tau):
+def cpu_baseline(w, q, k, v, tau, fractions=None):
     """Oracle (float64 NumPy) on a bounded sample: every step for about ten query heads (whole KV-head groups)."""
     from threadpoolctl import threadpool_info
     from oracle import psa_oracle as o
@@ -96,13 +99,73 @@ def cpu_baseline(w, q, k, v, tau):
     kh = k[:, :nkv].astype(np.float64)
     vh = v[:, :nkv].astype(np.float64)
     res = o.run_forward(qh, kh, vh, w.q_block, w.kv_block, tau, w.num_levels, w.scale, w.dtype,
-                        w.n_dense_prefix)
+                        w.n_dense_prefix, ranked_fractions=fractions)
     dt = time.perf_counter() - t0
     fl = o.effective_flops(res["mask"]["levels"], w.N, w.q_block, w.kv_block, w.d)
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{w.name}: all three steps (pyramid, mask, attention) for heads 0..{nh - 1} of {w.H}, "
                       f"{fl:.3e} effective FLOPs in {dt:.1f} s, float64 NumPy"}
+
+
+def compare_rules(psa, w, qd, kd, vd, steps: int):
+    """Output error against dense attention for four level-assignment rules at nearly equal
+    FLOP fractions: multi-level thresholds, multi-level ranked (matched block counts), and
+    their binary (one-level) forms keeping as many blocks as the multi-level masks' FLOPs
+    allow. Every step runs in the library's kernels; dense attention is the same attention
+    kernel with every block at level 0. Prints one JSON line."""
+    import torch
+    dev = qd.device
+    tau, fr = w.thresholds(), list(w.ranked_fractions())
+
+    def problem(L):
+        return psa.Problem(B=w.B, H=w.H, H_kv=w.H_kv, N=w.N, d=w.d, q_block=w.q_block, kv_block=w.kv_block,
+                           num_levels=L, dtype=w.dtype)
+
+    pL, p1 = problem(w.num_levels), problem(1)
+    k_pyr, v_pyr, k_bar = psa.psa_build_pyramid(pL, kd, vd)
+    dense_map = torch.zeros((w.B, w.H, pL.nqb, pL.nkb), dtype=torch.int8, device=dev)
+    o_dense, _ = psa.psa_attention_fwd(p1, qd, kd, vd, None, None, dense_map)
+    ref = o_dense.float()
+
+    def measure(prob, lm, kp, vp):
+        out, _ = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lm)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lm, o=out)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        x = out.float()
+        rel = float(torch.linalg.vector_norm(x - ref) / torch.linalg.vector_norm(ref))
+        cos = float(torch.nn.functional.cosine_similarity(x.reshape(-1, w.d), ref.reshape(-1, w.d), dim=1).mean())
+        lmh = lm.cpu().numpy()
+        rho = effective_flops(lmh, w.N, w.q_block, w.kv_block, w.d) / w.dense_flops()
+        return {"rho": round(rho, 5), "rel_l2_err": round(rel, 5), "mean_cos": round(cos, 6),
+                "attention_ms": round(ms, 4), "levels": level_histogram(lmh)}
+
+    res = {}
+    lm_t, _ = psa.psa_estimate_mask(pL, qd, k_bar, tau, w.n_dense_prefix)
+    res["multi-level thresholds"] = measure(pL, lm_t, k_pyr, v_pyr)
+    lm_r, _ = psa.psa_estimate_mask_ranked(pL, qd, k_bar, fr, w.n_dense_prefix)
+    res["multi-level ranked"] = measure(pL, lm_r, k_pyr, v_pyr)
+    # binary masks at the same FLOP fraction: keep rho * nkb blocks per row
+    rho_t = res["multi-level thresholds"]["rho"]
+    keep = int(round(rho_t * w.nkb))
+    lm_b, _ = psa.psa_estimate_mask_ranked(p1, qd, k_bar, [(keep + 0.5) / w.nkb], w.n_dense_prefix)
+    res["binary top-k"] = measure(p1, lm_b, None, None)
+    lo, hi = 0.0, 1.0                      # binary threshold with the same mean kept count
+    for _ in range(40):
+        mid = 0.5 * (lo + hi)
+        lm, _ = psa.psa_estimate_mask(p1, qd, k_bar, [mid], w.n_dense_prefix)
+        kept = float((lm >= 0).float().sum(-1).mean())
+        lo, hi = (mid, hi) if kept < keep else (lo, mid)
+    lm_bt, _ = psa.psa_estimate_mask(p1, qd, k_bar, [hi], w.n_dense_prefix)
+    res["binary threshold"] = measure(p1, lm_bt, None, None)
+    res["binary threshold"]["threshold"] = hi
+    print(json.dumps({"metric": "relative L2 error of O against dense attention at equal FLOP fraction",
+                      "workload": f"{w.name}: {w.description}", "data": "synthetic", "rules": res,
+                      "thresholds": list(tau), "fractions": fr, "binary_keep_blocks": keep}), flush=True)
 
 
 def main():
@@ -112,6 +175,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan13b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rule", choices=("threshold", "ranked"), default="threshold",
+                    help="level assignment: the workload's thresholds, or fixed shares of the ranked blocks")
+    ap.add_argument("--fractions", default=None,
+                    help="ranked rule: comma-separated cumulative block fractions per level "
+                         "(default: the workload's, matched to its threshold mask's mean level counts)")
+    ap.add_argument("--compare-rules", action="store_true",
+                    help="only compare the output error of threshold / ranked / binary masks at equal "
+                         "FLOP fraction against dense attention, print that JSON line and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -136,6 +207,10 @@ def main():
 
     w = get_workload(args.workload)
     tau = w.thresholds()
+    fractions = None
+    if args.rule == "ranked":
+        fractions = ([float(x) for x in args.fractions.split(",")] if args.fractions
+                     else list(w.ranked_fractions()))
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = generate(w, "q"), generate(w, "k"), generate(w, "v")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -143,6 +218,9 @@ def main():
     qd = torch.from_numpy(q).to(dt).to(dev)
     kd = torch.from_numpy(k).to(dt).to(dev)
     vd = torch.from_numpy(v).to(dt).to(dev)
+    if args.compare_rules:
+        compare_rules(psa, w, qd, kd, vd, args.steps)
+        return
     prob = psa.Problem(B=w.B, H=w.H, H_kv=w.H_kv, N=w.N, d=w.d, q_block=w.q_block, kv_block=w.kv_block,
                        num_levels=w.num_levels, dtype=w.dtype)
     R = prob.pyramid_rows
@@ -157,7 +235,11 @@ def main():
         if ev: ev[0].record()
         psa.psa_build_pyramid(prob, kd, vd, k_pyr, v_pyr, k_bar)
         if ev: ev[1].record()
-        psa.psa_estimate_mask(prob, qd, k_bar, tau, w.n_dense_prefix, level_map=level_map, workspace=ws)
+        if fractions is None:
+            psa.psa_estimate_mask(prob, qd, k_bar, tau, w.n_dense_prefix, level_map=level_map, workspace=ws)
+        else:
+            psa.psa_estimate_mask_ranked(prob, qd, k_bar, fractions, w.n_dense_prefix, level_map=level_map,
+                                         workspace=ws)
         if ev: ev[2].record()
         psa.psa_attention_fwd(prob, qd, kd, vd, k_pyr, v_pyr, level_map, o=o)
         if ev: ev[3].record()
@@ -197,7 +279,9 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "B": w.B, "H": w.H, "H_kv": w.H_kv,
                    "N": w.N, "d": w.d, "q_block": w.q_block, "kv_block": w.kv_block,
-                   "num_levels": w.num_levels, "thresholds": list(tau), "parallelism": "single GPU"},
+                   "num_levels": w.num_levels, "parallelism": "single GPU",
+                   **({"rule": "threshold", "thresholds": list(tau)} if fractions is None
+                      else {"rule": "ranked", "fractions": fractions})},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": attention_kernel_name(w.d, w.q_block, w.dtype)},
@@ -213,7 +297,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a head sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, tau)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, tau, fractions)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -9,6 +9,7 @@
  *
  *   psa_build_pyramid  — average-pooled K/V levels 1..L-1 and per-block mean keys
  *   psa_estimate_mask  — block importance and the threshold-based level map
+ *   psa_estimate_mask_ranked — the same with a fixed share of ranked blocks per level
  *   psa_attention_fwd  — attention over mixed-resolution keys, one softmax
  *
  * Tensors (all row-major, contiguous, head_dim innermost):
@@ -26,7 +27,7 @@
  *  - Device pointers point to memory of the current HIP device; the caller owns
  *    every buffer, keeps it alive until the work on `stream` has finished, and the
  *    library keeps no pointer after a call returns. Device pointers must be
- *    16-byte aligned. `thresholds` is a host pointer.
+ *    16-byte aligned. `thresholds` and `fractions` are host pointers.
  *  - Calls only enqueue kernels on `stream` and return without synchronising.
  *    The library holds no state and allocates no memory; calls are thread-safe.
  *  - Arguments are checked before anything is launched: invalid values return
@@ -120,6 +121,25 @@ psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const f
                                const float* thresholds, int32_t n_dense_prefix,
                                int8_t* level_map, float* cmass_out,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Step 2 with the ranked (quantile) rule in place of thresholds: the alternative
+ * assignment the top168.com ablation paragraph compares with thresholds; a fixed
+ * share of the score-ranked blocks at full resolution and the rest spread over the
+ * pooled levels (skillmd.com page, "Level assignment", whose keep ratio is
+ * fractions[0]). With num_levels == 1 it is the binary top-k block-sparse mask.
+ * Scores and ranking are those of psa_estimate_mask. With K_l = floor(fractions[l]
+ * * nkb) (the product in double precision), the block of rank r (0 = most
+ * important) gets level_ij = min{l : r < K_l}, or -1 (pruned) if there is none.
+ * So each row has K_l - K_{l-1} blocks at level l (K_{-1} = 0) before the dense
+ * prefix is applied as in psa_estimate_mask. cmass_out (nullable): C as defined there.
+ * fractions: host array of num_levels doubles, nondecreasing, each in [0, 1].
+ * Workspace, supported sizes and errors as psa_estimate_mask.
+ */
+psa_status_t psa_estimate_mask_ranked(const psa_problem_t* prob, const void* q, const float* k_bar,
+                                      const double* fractions, int32_t n_dense_prefix,
+                                      int8_t* level_map, float* cmass_out,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Step 3, attention over mixed-resolution keys with one softmax ("adaptive

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpsa.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m level_pooled_kv_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python level_pooled_kv_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -32,7 +32,7 @@ PSA_WS_ESTIMATE_MASK, PSA_WS_ATTENTION_FWD = 0, 1
 
 EXPORTED = (
     "psa_pyramid_rows", "psa_workspace_bytes", "psa_check_problem", "psa_build_pyramid",
-    "psa_estimate_mask", "psa_attention_fwd", "psa_status_string", "psa_last_error",
+    "psa_estimate_mask", "psa_estimate_mask_ranked", "psa_attention_fwd", "psa_status_string", "psa_last_error",
 )
 
 
@@ -55,6 +55,9 @@ _lib.psa_build_pyramid.restype = _st
 _lib.psa_estimate_mask.argtypes = [_P, _vp, _vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int32, _vp, _vp,
                                    _vp, _sz, _vp]
 _lib.psa_estimate_mask.restype = _st
+_lib.psa_estimate_mask_ranked.argtypes = [_P, _vp, _vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int32, _vp,
+                                          _vp, _vp, _sz, _vp]
+_lib.psa_estimate_mask_ranked.restype = _st
 _lib.psa_attention_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.psa_attention_fwd.restype = _st
 _lib.psa_status_string.argtypes, _lib.psa_status_string.restype = [_st], ctypes.c_char_p
@@ -151,12 +154,7 @@ def psa_build_pyramid(prob: Problem, k: torch.Tensor, v: torch.Tensor, k_pyr: Op
     return k_pyr, v_pyr, k_bar
 
 
-def psa_estimate_mask(prob: Problem, q: torch.Tensor, k_bar: torch.Tensor, thresholds: Sequence[float],
-                      n_dense_prefix: int = 0, level_map: Optional[torch.Tensor] = None,
-                      cmass: Optional[torch.Tensor] = None, want_cmass: bool = False,
-                      workspace: Optional[torch.Tensor] = None, stream=None):
-    """Step 2: level map [B,H,nqb,nkb] int8 (-1 = pruned); optionally the float32 cumulative mass.
-    Returns (level_map, cmass or None)."""
+def _mask_buffers(prob: Problem, q, k_bar, level_map, cmass, want_cmass, workspace):
     _need(q, "q", (prob.B, prob.H, prob.N, prob.d), prob.torch_dtype)
     _need(k_bar, "k_bar", (prob.B, prob.H_kv, prob.nkb, prob.d), torch.float32)
     shape = (prob.B, prob.H, prob.nqb, prob.nkb)
@@ -165,13 +163,45 @@ def psa_estimate_mask(prob: Problem, q: torch.Tensor, k_bar: torch.Tensor, thres
     _need(level_map, "level_map", shape, torch.int8)
     if cmass is None and want_cmass:
         cmass = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if cmass is not None:
+        _need(cmass, "cmass", shape, torch.float32)
     ws_bytes = prob.workspace_bytes(PSA_WS_ESTIMATE_MASK)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    tau = (ctypes.c_float * len(thresholds))(*[float(t) for t in thresholds])
+    return level_map, cmass, workspace
+
+
+def _per_level(prob: Problem, values: Sequence[float], name: str, ctype):
+    if len(values) < prob.num_levels:
+        raise ValueError(f"{name}: {len(values)} values for {prob.num_levels} levels")
+    return (ctype * len(values))(*[float(x) for x in values])
+
+
+def psa_estimate_mask(prob: Problem, q: torch.Tensor, k_bar: torch.Tensor, thresholds: Sequence[float],
+                      n_dense_prefix: int = 0, level_map: Optional[torch.Tensor] = None,
+                      cmass: Optional[torch.Tensor] = None, want_cmass: bool = False,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Step 2: level map [B,H,nqb,nkb] int8 (-1 = pruned); optionally the float32 cumulative mass.
+    Returns (level_map, cmass or None)."""
+    level_map, cmass, workspace = _mask_buffers(prob, q, k_bar, level_map, cmass, want_cmass, workspace)
+    tau = _per_level(prob, thresholds, "thresholds", ctypes.c_float)
     _check(_lib.psa_estimate_mask(ctypes.byref(prob.c()), _ptr(q), _ptr(k_bar), tau, int(n_dense_prefix),
                                   _ptr(level_map), _ptr(cmass), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return level_map, cmass
+
+
+def psa_estimate_mask_ranked(prob: Problem, q: torch.Tensor, k_bar: torch.Tensor, fractions: Sequence[float],
+                             n_dense_prefix: int = 0, level_map: Optional[torch.Tensor] = None,
+                             cmass: Optional[torch.Tensor] = None, want_cmass: bool = False,
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Step 2, ranked rule: the top floor(fractions[l] * nkb) blocks of each row take level l
+    or a finer one. Returns (level_map, cmass or None)."""
+    level_map, cmass, workspace = _mask_buffers(prob, q, k_bar, level_map, cmass, want_cmass, workspace)
+    fr = _per_level(prob, fractions, "fractions", ctypes.c_double)
+    _check(_lib.psa_estimate_mask_ranked(ctypes.byref(prob.c()), _ptr(q), _ptr(k_bar), fr, int(n_dense_prefix),
+                                         _ptr(level_map), _ptr(cmass), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
     return level_map, cmass
 
 

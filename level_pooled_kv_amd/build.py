@@ -1,6 +1,8 @@
 """Build libpsa.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m level_pooled_kv_amd.build
+    python level_pooled_kv_amd/build.py
+
+(run as a file: importing the package would load the library it rebuilds)
 
 Objects go to _build/ at the repository root; the library is written next to
 this file so it travels with the source tree.

@@ -151,27 +151,17 @@ psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const v
   return hip_status(psa::launch_pyramid(a, stream), "psa_build_pyramid launch");
 }
 
-psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const float* k_bar,
-                               const float* thresholds, int32_t n_dense_prefix, int8_t* level_map,
-                               float* cmass_out, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
-  clear_error();
-  psa_status_t s = check_problem(prob);
-  if (s != PSA_OK) return s;
+// Checks shared by both mask entry points, then the launch. Exactly one of tau and
+// counts is non-NULL: the threshold rule or the ranked rule.
+static psa_status_t estimate_mask_common(const psa_problem_t* prob, const void* q, const float* k_bar,
+                                         int32_t n_dense_prefix, int8_t* level_map, float* cmass_out,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                         const float* tau, const int* counts, const char* what) {
   REQUIRE_PTR(q, "q");
   REQUIRE_PTR(k_bar, "k_bar");
   REQUIRE_PTR(level_map, "level_map");
   if (cmass_out && !aligned16(cmass_out))
     return fail(PSA_ERR_INVALID_ARGUMENT, "cmass_out is not 16-byte aligned");
-  if (!thresholds) return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds is NULL");
-  for (int l = 0; l < prob->num_levels; ++l) {
-    const float t = thresholds[l];
-    if (!(t >= 0.f && t <= 1.f))
-      return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds[%d] = %g is not in [0, 1]", l, (double)t);
-    if (l > 0 && t < thresholds[l - 1])
-      return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds must be nondecreasing (thresholds[%d] < thresholds[%d])",
-                  l, l - 1);
-  }
   if (n_dense_prefix < 0 || n_dense_prefix > prob->N)
     return fail(PSA_ERR_INVALID_ARGUMENT, "n_dense_prefix %d not in [0, N]", n_dense_prefix);
   const size_t need = mask_workspace(prob);
@@ -190,8 +180,55 @@ psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const f
   a.n_dense_prefix = n_dense_prefix;
   a.bf16 = prob->dtype == PSA_BF16;
   a.scale = effective_scale(prob);
-  for (int l = 0; l < psa::kMaxLevels; ++l) a.tau[l] = l < prob->num_levels ? thresholds[l] : 0.f;
-  return hip_status(psa::launch_mask(a, stream), "psa_estimate_mask launch");
+  a.ranked = counts != nullptr;
+  for (int l = 0; l < psa::kMaxLevels; ++l) {
+    a.tau[l] = tau && l < prob->num_levels ? tau[l] : 0.f;
+    a.rank_count[l] = counts && l < prob->num_levels ? counts[l] : 0;
+  }
+  return hip_status(psa::launch_mask(a, stream), what);
+}
+
+psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const float* k_bar,
+                               const float* thresholds, int32_t n_dense_prefix, int8_t* level_map,
+                               float* cmass_out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  clear_error();
+  psa_status_t s = check_problem(prob);
+  if (s != PSA_OK) return s;
+  if (!thresholds) return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds is NULL");
+  for (int l = 0; l < prob->num_levels; ++l) {
+    const float t = thresholds[l];
+    if (!(t >= 0.f && t <= 1.f))
+      return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds[%d] = %g is not in [0, 1]", l, (double)t);
+    if (l > 0 && t < thresholds[l - 1])
+      return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds must be nondecreasing (thresholds[%d] < thresholds[%d])",
+                  l, l - 1);
+  }
+  return estimate_mask_common(prob, q, k_bar, n_dense_prefix, level_map, cmass_out, workspace, workspace_bytes,
+                              stream, thresholds, nullptr, "psa_estimate_mask launch");
+}
+
+psa_status_t psa_estimate_mask_ranked(const psa_problem_t* prob, const void* q, const float* k_bar,
+                                      const double* fractions, int32_t n_dense_prefix, int8_t* level_map,
+                                      float* cmass_out, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  clear_error();
+  psa_status_t s = check_problem(prob);
+  if (s != PSA_OK) return s;
+  if (!fractions) return fail(PSA_ERR_INVALID_ARGUMENT, "fractions is NULL");
+  const int64_t nkb = ceil_div(prob->N, psa::kKvBlock);
+  int counts[psa::kMaxLevels] = {0, 0, 0, 0};
+  for (int l = 0; l < prob->num_levels; ++l) {
+    const double f = fractions[l];
+    if (!(f >= 0.0 && f <= 1.0))
+      return fail(PSA_ERR_INVALID_ARGUMENT, "fractions[%d] = %g is not in [0, 1]", l, f);
+    if (l > 0 && f < fractions[l - 1])
+      return fail(PSA_ERR_INVALID_ARGUMENT, "fractions must be nondecreasing (fractions[%d] < fractions[%d])",
+                  l, l - 1);
+    counts[l] = (int)floor(f * (double)nkb);   // in [0, nkb]
+  }
+  return estimate_mask_common(prob, q, k_bar, n_dense_prefix, level_map, cmass_out, workspace, workspace_bytes,
+                              stream, nullptr, counts, "psa_estimate_mask_ranked launch");
 }
 
 psa_status_t psa_attention_fwd(const psa_problem_t* prob, const void* q, const void* k, const void* v,

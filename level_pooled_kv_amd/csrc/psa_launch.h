@@ -27,6 +27,8 @@ struct MaskArgs {
   bool bf16;
   float scale;
   float tau[kMaxLevels];
+  bool ranked;                   // level by rank: rank < rank_count[l] instead of C < tau[l]
+  int rank_count[kMaxLevels];    // cumulative block counts of the ranked rule (0 past L)
 };
 
 struct AttnArgs {

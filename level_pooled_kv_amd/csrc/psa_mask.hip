@@ -20,6 +20,11 @@
 //    partners in other lanes come through cross-lane shuffles, so no LDS and no
 //    workgroup barrier), a wave-wide exclusive scan of the masses in rank order,
 //    the threshold compares and the int8 level writes.
+//    Its ranked form (the quantile rule the top168.com ablation compares with
+//    thresholds; fixed shares of the score-ranked blocks per level: skillmd.com,
+//    "Level assignment") gives the block at rank r the lowest level l with
+//    r < K_l for host-computed cumulative counts K_l, so it needs the sort but
+//    neither the softmax nor the scan.
 #include "psa_device.h"
 #include "psa_launch.h"
 
@@ -321,11 +326,11 @@ __device__ __forceinline__ float wave_exclusive_sum(float tot, int lane) {
 // block index) and calls that want the cumulative mass itself take the exact path:
 // a sort of 64-bit (score, index) keys. Both paths sum the same masses in the same
 // order, so they give the same levels.
-template <int E>
+template <int E, bool RANKED>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
                    int N, int nkb, int nrows, int L, int n_dense_prefix,
-                   float tau0, float tau1, float tau2, float tau3) {
+                   float tau0, float tau1, float tau2, float tau3, int4 kcut) {
   constexpr int NP = 64 * E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * (kMaskThreads / 64) + wave;
@@ -343,19 +348,23 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     for (int r = 0; r < E; ++r) zz[r] = zr[r];
   }
 
-  // ---- softmax statistics of the row
-  float mx = -INFINITY;
+  // ---- softmax statistics of the row (the ranked rule needs them only for cmass)
+  const bool want_mass = !RANKED || cmass != nullptr;
+  float mx = -INFINITY, inv_s = 0.f;
+  if (want_mass) {
 #pragma unroll
-  for (int r = 0; r < E; ++r)
-    if (E * lane + r < nkb) mx = fmaxf(mx, zz[r]);
-  mx = wave_max(mx);
-  float s = 0.f;
+    for (int r = 0; r < E; ++r)
+      if (E * lane + r < nkb) mx = fmaxf(mx, zz[r]);
+    mx = wave_max(mx);
+    float s = 0.f;
 #pragma unroll
-  for (int r = 0; r < E; ++r)
-    if (E * lane + r < nkb) s += __expf(zz[r] - mx);
-  s = wave_sum(s);
-  const float inv_s = 1.0f / s;
+    for (int r = 0; r < E; ++r)
+      if (E * lane + r < nkb) s += __expf(zz[r] - mx);
+    s = wave_sum(s);
+    inv_s = 1.0f / s;
+  }
   const float tau[4] = {tau0, tau1, tau2, tau3};
+  const int K[4] = {kcut.x, kcut.y, kcut.z, kcut.w};
   int8_t* lrow = level_map + (int64_t)row * nkb;
 
   if (cmass == nullptr) {
@@ -372,21 +381,27 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
     tie |= lane < 63 && key[E - 1] == next_first && key[E - 1] != kPadKey32;
     if (__ballot(tie) == 0) {
-      float p[E], tot = 0.f;
-#pragma unroll
-      for (int r = 0; r < E; ++r) {
-        p[r] = key[r] != kPadKey32 ? __expf(key32_score(key[r]) - mx) * inv_s : 0.f;
-        tot += p[r];
-      }
-      float run = wave_exclusive_sum(tot, lane);
+      // cnt[l]: how many blocks, in rank order, take level l or a finer one
       int cnt[kMaxLevels] = {0, 0, 0, 0};
+      if constexpr (RANKED) {
 #pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const float C = run;
-        run += p[r];
-        const bool real = key[r] != kPadKey32;
+        for (int l = 0; l < kMaxLevels; ++l) cnt[l] = K[l];
+      } else {
+        float p[E], tot = 0.f;
 #pragma unroll
-        for (int l = 0; l < kMaxLevels; ++l) cnt[l] += (int)__popcll(__ballot(real && C < tau[l]));
+        for (int r = 0; r < E; ++r) {
+          p[r] = key[r] != kPadKey32 ? __expf(key32_score(key[r]) - mx) * inv_s : 0.f;
+          tot += p[r];
+        }
+        float run = wave_exclusive_sum(tot, lane);
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const float C = run;
+          run += p[r];
+          const bool real = key[r] != kPadKey32;
+#pragma unroll
+          for (int l = 0; l < kMaxLevels; ++l) cnt[l] += (int)__popcll(__ballot(real && C < tau[l]));
+        }
       }
       // key at sorted position cnt[l] - 1: the last block level l (or a lower one) takes
       uint32_t cut[kMaxLevels];
@@ -427,10 +442,10 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const uint32_t j = (uint32_t)key[r];
-    p[r] = j < (uint32_t)nkb ? __expf(key_score(key[r]) - mx) * inv_s : 0.f;
+    p[r] = want_mass && j < (uint32_t)nkb ? __expf(key_score(key[r]) - mx) * inv_s : 0.f;
     tot += p[r];
   }
-  float run = wave_exclusive_sum(tot, lane);
+  float run = want_mass ? wave_exclusive_sum(tot, lane) : 0.f;
   float* crow = cmass ? cmass + (int64_t)row * nkb : nullptr;
 #pragma unroll
   for (int r = 0; r < E; ++r) {
@@ -440,8 +455,10 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     if (j < (uint32_t)nkb) {
       int lev = -1;
 #pragma unroll
-      for (int l = kMaxLevels - 1; l >= 0; --l)
-        if (l < L && C < tau[l]) lev = l;
+      for (int l = kMaxLevels - 1; l >= 0; --l) {
+        const bool in = RANKED ? E * lane + r < K[l] : C < tau[l];   // sorted position = rank
+        if (l < L && in) lev = l;
+      }
       if (64 * (int)j < n_dense_prefix) lev = 0;
       lrow[j] = (int8_t)lev;
       if (crow) crow[j] = C;
@@ -456,11 +473,18 @@ int mask_score_stride(int nkb) {
   return n;
 }
 
+template <int E, bool RANKED>
+static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
+  const int4 kcut = make_int4(a.rank_count[0], a.rank_count[1], a.rank_count[2], a.rank_count[3]);
+  hipLaunchKernelGGL((block_level_kernel<E, RANKED>), dim3((nrows + 3) / 4), dim3(kMaskThreads), 0, stream,
+                     a.z, a.level_map, a.cmass, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0], a.tau[1],
+                     a.tau[2], a.tau[3], kcut);
+}
+
 template <int E>
 static void launch_level_e(const MaskArgs& a, int nrows, hipStream_t stream) {
-  hipLaunchKernelGGL((block_level_kernel<E>), dim3((nrows + 3) / 4), dim3(kMaskThreads), 0, stream, a.z,
-                     a.level_map, a.cmass, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0], a.tau[1],
-                     a.tau[2], a.tau[3]);
+  if (a.ranked) launch_level_r<E, true>(a, nrows, stream);
+  else launch_level_r<E, false>(a, nrows, stream);
 }
 
 template <typename T, int D>

@@ -10,7 +10,15 @@ non-increasing in x, so bisection on log x finds x with |rho - target| <= 0.005
 on the oracle's mask of the workload's seeded inputs. The thresholds are stored
 as float32 values, since that is what the library receives.
 
+With --ranked it instead matches the ranked rule to the stored thresholds: the
+cumulative fraction of level l is the mean, over the query-block rows of the
+threshold mask (before the dense prefix is forced), of the number of blocks at
+level <= l, rounded to a whole count c and stored as (c + 0.5) / nkb so that
+floor(f * nkb) = c exactly. Both rules then keep the same mean number of blocks
+per level, which puts them at nearly equal FLOP fractions.
+
     python -m oracle.calibrate_thresholds [workload ...]
+    python -m oracle.calibrate_thresholds --ranked [workload ...]
 """
 from __future__ import annotations
 
@@ -75,14 +83,36 @@ def calibrate(w: W.Workload, tol: float = 0.005):
     return {"x": x, "thresholds": list(tau), "rho": r, "target_rho": w.target_rho}
 
 
+def match_ranked(w: W.Workload, entry: dict) -> dict:
+    t0 = time.time()
+    qbar, kbar = block_means_streamed(w)
+    z = o.block_scores(qbar, kbar, o.block_sizes(w.N, w.kv_block), w.scale)
+    C = o.cumulative_mass(z, o.softmax_rows(z))
+    tau = entry["thresholds"]
+    lev = o.assign_levels(C, tau, w.num_levels, 0, w.kv_block)
+    fr = []
+    for l in range(w.num_levels):
+        c = int(round(float(((lev >= 0) & (lev <= l)).sum(axis=-1).mean())))
+        fr.append((c + 0.5) / w.nkb)
+    lev_r = o.assign_levels_ranked(z, fr, w.num_levels, w.n_dense_prefix, w.kv_block)
+    r = o.effective_flops(lev_r, w.N, w.q_block, w.kv_block, w.d) / w.dense_flops()
+    print(f"{w.name}: ranked fractions {fr} rho={r:.5f} (thresholds: {entry['rho']:.5f}) "
+          f"in {time.time()-t0:.1f}s", flush=True)
+    out = dict(entry)
+    out.update({"ranked_fractions": fr, "ranked_rho": r})
+    return out
+
+
 def main(argv):
+    ranked = "--ranked" in argv
+    argv = [a for a in argv if a != "--ranked"]
     names = argv or [n for n, w in W.WORKLOADS.items() if w.target_rho is not None]
     table = {}
     if os.path.exists(W.THRESHOLDS_FILE):
         with open(W.THRESHOLDS_FILE) as f:
             table = json.load(f)
     for n in names:
-        table[n] = calibrate(W.WORKLOADS[n])
+        table[n] = match_ranked(W.WORKLOADS[n], table[n]) if ranked else calibrate(W.WORKLOADS[n])
         with open(W.THRESHOLDS_FILE, "w") as f:
             json.dump(table, f, indent=2, sort_keys=True)
             f.write("\n")

@@ -399,12 +399,16 @@ def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, 
 
 
 def run_forward(q, k, v, q_block, kv_block, thresholds, num_levels, scale, io_dtype,
-                n_dense_prefix=0, items=None):
-    """All three steps chained: pyramid (rounded to the I/O dtype), mask, attention."""
+                n_dense_prefix=0, items=None, ranked_fractions=None):
+    """All three steps chained: pyramid (rounded to the I/O dtype), mask, attention.
+    With ranked_fractions the mask takes the ranked rule instead of the thresholds."""
     kp = build_pyramid(k, num_levels)
     vp = build_pyramid(v, num_levels)
     kp_io = [np.asarray(k, np.float64)] + [round_to_io(x, io_dtype) for x in kp[1:]]
     vp_io = [np.asarray(v, np.float64)] + [round_to_io(x, io_dtype) for x in vp[1:]]
-    mask = estimate_mask(q, k, q_block, kv_block, thresholds, num_levels, scale, n_dense_prefix)
+    if ranked_fractions is None:
+        mask = estimate_mask(q, k, q_block, kv_block, thresholds, num_levels, scale, n_dense_prefix)
+    else:
+        mask = estimate_mask_ranked(q, k, q_block, kv_block, ranked_fractions, num_levels, scale, n_dense_prefix)
     O, LSE = pyramid_attention(q, kp_io, vp_io, mask["levels"], q_block, kv_block, scale, items)
     return {"kpyr": kp_io, "vpyr": vp_io, "mask": mask, "O": O, "LSE": LSE}

@@ -8,8 +8,9 @@ The host models they imitate are the ones the top168.com article names in its
 results paragraphs (Wan2.1-1.3B / 14B, CogVideoX-5B, Qwen2.5-VL-7B).
 
 This module holds data only: no step of the method's arithmetic lives here.
-Thresholds for the four sparsity-targeted workloads are read from
-``thresholds.json``, which the oracle's calibration script writes.
+Thresholds for the four sparsity-targeted workloads (and the ranked rule's
+matched block fractions) are read from ``thresholds.json``, which the oracle's
+calibration script writes.
 """
 from __future__ import annotations
 
@@ -74,6 +75,15 @@ class Workload:
         if entry is None:
             raise KeyError(f"no calibrated thresholds for workload {self.name!r} in {THRESHOLDS_FILE}")
         return tuple(float(t) for t in entry["thresholds"][: self.num_levels])
+
+    def ranked_fractions(self) -> Tuple[float, ...]:
+        """Cumulative block fractions per level for the ranked rule, matched to the
+        threshold mask's mean level counts (written by the same calibration script)."""
+        with open(THRESHOLDS_FILE) as f:
+            entry = json.load(f).get(self.name, {})
+        if "ranked_fractions" not in entry:
+            raise KeyError(f"no ranked fractions for workload {self.name!r} in {THRESHOLDS_FILE}")
+        return tuple(float(x) for x in entry["ranked_fractions"][: self.num_levels])
 
     def dense_flops(self) -> float:
         """4*B*H*N^2*d: QK^T plus PV of dense attention."""

@@ -9,6 +9,8 @@ Tolerances:
     [C_lo - 1e-5, C_hi + 1e-5], where C_lo / C_hi are the oracle's mass ahead of j
     if every block whose score is within 1e-6*|z_j| of z_j were ranked behind /
     ahead of j (so: within 1e-5 of a threshold, or a near-tie reordering);
+  * ranked level map: exact per-level counts in every row; a mismatch only where a
+    near-tie (scores within 1e-6 relative) could move the block across a count;
   * attention output: max |gpu - oracle| <= 2e-2, mean <= 2e-3, no NaN.
 """
 from __future__ import annotations
@@ -97,6 +99,51 @@ def check_mask(gpu_levels: np.ndarray, ora: dict, tau, L: int, n_dense_prefix: i
         gl = L if gl < 0 else gl
         if not (finest <= gl <= coarsest):
             bad.append((int(b), int(h), int(i), int(j), int(ref[b, h, i, j]), gl, float(C[b, h, i, j])))
+    assert not bad, (label, f"{len(bad)} unaccepted level mismatches, first: {bad[:5]}")
+    return len(diff)
+
+
+def check_mask_ranked(gpu_levels: np.ndarray, ora: dict, counts, L: int, n_dense_prefix: int,
+                      kv_block: int = 64, label: str = ""):
+    """Ranked rule. Every row must hold exactly K_l - K_{l-1} blocks at level l (checked
+    on rows without forced blocks) -- unique whatever the order of near-ties. A block
+    may differ from the oracle only when its level is the rule's level for some rank in
+    [r_lo, r_hi], where r_lo / r_hi count the other blocks whose score is above
+    z_j + 1e-6*|z_j| / at least z_j - 1e-6*|z_j| (a near-tie reordering).
+    Returns the number of accepted mismatches."""
+    ref = ora["levels"]
+    assert gpu_levels.shape == ref.shape, (label, gpu_levels.shape, ref.shape)
+    K = list(counts[:L])
+
+    def level_of_rank(r):
+        for l in range(L):
+            if r < K[l]:
+                return l
+        return L
+
+    if n_dense_prefix == 0:
+        flat = gpu_levels.reshape(-1, gpu_levels.shape[-1])
+        for l in range(L):
+            want = K[l] - (K[l - 1] if l else 0)
+            have = (flat == l).sum(axis=1)
+            assert np.all(have == max(want, 0)), (label, l, want, np.unique(have))
+    nforce = -(-n_dense_prefix // kv_block) if n_dense_prefix > 0 else 0
+    z = ora["z"]
+    bad = []
+    diff = np.argwhere(gpu_levels != ref)
+    for (b, h, i, j) in diff:
+        if j < nforce:
+            bad.append((b, h, i, j, "forced block"))
+            continue
+        zr = z[b, h, i]
+        delta = MASK_Z_REL * abs(zr[j])
+        others = np.arange(len(zr)) != j
+        r_lo = int(((zr > zr[j] + delta) & others).sum())
+        r_hi = int(((zr >= zr[j] - delta) & others).sum())
+        gl = int(gpu_levels[b, h, i, j])
+        gl = L if gl < 0 else gl
+        if not (level_of_rank(r_lo) <= gl <= level_of_rank(r_hi)):
+            bad.append((int(b), int(h), int(i), int(j), int(ref[b, h, i, j]), gl, r_lo, r_hi))
     assert not bad, (label, f"{len(bad)} unaccepted level mismatches, first: {bad[:5]}")
     return len(diff)
 

@@ -118,6 +118,33 @@ def test_estimate_mask_rejects(psa):
     assert f(ctypes.byref(c), FAKE, FAKE, ok_tau, 0, FAKE, MISALIGNED, FAKE, ws, None) == 1
 
 
+def fracs(*vals):
+    return (ctypes.c_double * len(vals))(*vals)
+
+
+def test_estimate_mask_ranked_rejects(psa):
+    p = prob(psa)
+    c = p.c()
+    ws = p.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
+    f = psa.lib.psa_estimate_mask_ranked
+    ok = fracs(0.1, 0.4, 0.7, 1.0)
+    # fractions: NaN, out of range, decreasing, NULL
+    for fr in (fracs(0.1, float("nan"), 0.7, 1.0), fracs(-0.01, 0.4, 0.7, 1.0), fracs(0.1, 0.4, 0.7, 1.01),
+               fracs(0.4, 0.1, 0.7, 1.0)):
+        assert f(ctypes.byref(c), FAKE, FAKE, fr, 0, FAKE, None, FAKE, ws, None) == 1
+        assert "fractions" in psa.last_error()
+    assert f(ctypes.byref(c), FAKE, FAKE, None, 0, FAKE, None, FAKE, ws, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, ok, -1, FAKE, None, FAKE, ws, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, ok, 0, FAKE, None, FAKE, ws - 1, None) == 3
+    assert f(ctypes.byref(c), FAKE, FAKE, ok, 0, None, None, FAKE, ws, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, ok, 0, FAKE, MISALIGNED, FAKE, ws, None) == 1
+    # only the first num_levels fractions are read
+    c2 = prob(psa, num_levels=2).c()
+    assert f(ctypes.byref(c2), FAKE, FAKE, fracs(0.1, 0.4, float("nan"), -3.0), 0, FAKE, MISALIGNED, FAKE, ws,
+             None) == 1
+    assert "cmass_out" in psa.last_error()
+
+
 def test_attention_rejects(psa):
     c = prob(psa).c()
     f = psa.lib.psa_attention_fwd
