@@ -15,7 +15,8 @@ method as the pages describe it:
   (progressive pooling, a multi-level mask generator driven by query-block /
   KV-block importance, attention that keeps the probability distribution
   consistent); ablation paragraph (threshold-based assignment preferred to
-  quantile-based; multi-level masks preferred to binary ones).
+  quantile-based; multi-level masks preferred to binary ones); paragraph on
+  causal use (generation) and bidirectional use (understanding).
 * skillmd.com "Psa Pyramid Sparse Attention", sections "Pooled KV cache
   creation" (pool factor 2**level, average pooling over tokens), "Block
   importance scoring" (query against the block's mean key) and "Level
@@ -226,17 +227,54 @@ def assign_levels(C: np.ndarray, thresholds: Sequence[float], num_levels: int,
 
 def estimate_mask(q: np.ndarray, k: np.ndarray, q_block: int, kv_block: int,
                   thresholds: Sequence[float], num_levels: int, scale: float,
-                  n_dense_prefix: int = 0) -> Dict[str, np.ndarray]:
-    """The whole mask step: q/k [B,H(_kv),N,d] -> level map [B,H,nqb,nkb] int8 (+ intermediates)."""
+                  n_dense_prefix: int = 0, causal: bool = False) -> Dict[str, np.ndarray]:
+    """The whole mask step: q/k [B,H(_kv),N,d] -> level map [B,H,nqb,nkb] int8 (+ intermediates).
+    causal: see causal_blocks and apply_causal."""
     N = q.shape[-2]
     qbar = block_means(q, q_block)
     kbar = block_means(k, kv_block)
     n_kv = block_sizes(N, kv_block)
     z = block_scores(qbar, kbar, n_kv, scale)
+    if causal:
+        vis, _ = causal_blocks(N, q_block, kv_block)
+        z = np.where(vis, z, -np.inf)
     p = softmax_rows(z)
     C = cumulative_mass(z, p)
     lev = assign_levels(C, thresholds, num_levels, n_dense_prefix, kv_block)
+    if causal:
+        C, lev = apply_causal(C, lev, N, q_block, kv_block)
     return {"qbar": qbar, "kbar": kbar, "z": z, "p": p, "cmass": C, "levels": lev}
+
+
+# ----------------------------------------------------------------------------
+# Causal use (top168.com article, paragraph on causal and bidirectional use)
+# ----------------------------------------------------------------------------
+
+def causal_blocks(N: int, q_block: int, kv_block: int) -> Tuple[np.ndarray, np.ndarray]:
+    """vis[i, j]: KV block j holds a token at or before the last row of query block i;
+    diag[i, j]: it is visible and holds a token at or after the block's first row (so it
+    is not entirely in the past of every row of the block)."""
+    nqb, nkb = -(-N // q_block), -(-N // kv_block)
+    r0 = np.arange(nqb)[:, None] * q_block
+    r1 = np.minimum(r0 + q_block, N)
+    j0 = np.arange(nkb)[None, :] * kv_block
+    j1 = np.minimum(j0 + kv_block, N)
+    vis = j0 <= r1 - 1
+    diag = vis & (j1 - 1 >= r0)
+    return vis, diag
+
+
+def apply_causal(C: np.ndarray, lev: np.ndarray, N: int, q_block: int, kv_block: int):
+    """Causal reading of the mask: the mass and ranking run over the visible blocks only
+    (the caller gives invisible blocks z = -inf); a block that reaches the query block's
+    own rows is kept at full resolution, since a pooled key mixing in later tokens would
+    leak them; invisible blocks are pruned and report C = 1 (all mass lies ahead)."""
+    vis, diag = causal_blocks(N, q_block, kv_block)
+    C = np.where(vis, C, 1.0)
+    lev = lev.copy()
+    lev[..., diag] = 0
+    lev[..., ~vis] = -1
+    return C, lev
 
 
 # ----------------------------------------------------------------------------
@@ -262,19 +300,25 @@ def block_ranks(z: np.ndarray) -> np.ndarray:
 
 
 def assign_levels_ranked(z: np.ndarray, fractions: Sequence[float], num_levels: int,
-                         n_dense_prefix: int = 0, kv_block: int = 64) -> np.ndarray:
+                         n_dense_prefix: int = 0, kv_block: int = 64, n_rank=None) -> np.ndarray:
     """level_j = min{l : rank_j < K_l}, or -1 (pruned) if no level qualifies; then the
     KV blocks overlapping tokens [0, n_dense_prefix) are set to level 0.
 
     The pages rank blocks by score and give fixed shares of them to each level
     (skillmd.com "Level assignment"; the top168.com ablation calls this the
     quantile-based rule). Reading: the blocks left after the keep ratio are taken
-    in importance order, so a less important block never gets a finer level."""
-    K = rank_counts(fractions, num_levels, z.shape[-1])
+    in importance order, so a less important block never gets a finer level.
+
+    n_rank: number of blocks the counts are taken of, per query-block row (broadcast
+    against z[..., 0]); default: all nkb blocks."""
     rank = block_ranks(z)
     lev = np.full(z.shape, -1, dtype=np.int8)
+    if n_rank is None:
+        n_rank = np.full(z.shape[:-1], z.shape[-1])
+    n_rank = np.broadcast_to(np.asarray(n_rank), z.shape[:-1])
     for l in range(num_levels - 1, -1, -1):
-        lev[rank < K[l]] = l
+        K = np.vectorize(lambda n: rank_counts(fractions, num_levels, int(n))[l])(n_rank)
+        lev[rank < np.asarray(K)[..., None]] = l
     if n_dense_prefix > 0:
         nforce = -(-n_dense_prefix // kv_block)
         lev[..., :nforce] = 0
@@ -283,15 +327,23 @@ def assign_levels_ranked(z: np.ndarray, fractions: Sequence[float], num_levels: 
 
 def estimate_mask_ranked(q: np.ndarray, k: np.ndarray, q_block: int, kv_block: int,
                          fractions: Sequence[float], num_levels: int, scale: float,
-                         n_dense_prefix: int = 0) -> Dict[str, np.ndarray]:
-    """The mask step with the ranked rule; scores, p and C as in estimate_mask."""
+                         n_dense_prefix: int = 0, causal: bool = False) -> Dict[str, np.ndarray]:
+    """The mask step with the ranked rule; scores, p and C as in estimate_mask. Causal:
+    the counts are fractions of each row's visible blocks, then apply_causal."""
     N = q.shape[-2]
     qbar = block_means(q, q_block)
     kbar = block_means(k, kv_block)
     z = block_scores(qbar, kbar, block_sizes(N, kv_block), scale)
+    n_rank = None
+    if causal:
+        vis, _ = causal_blocks(N, q_block, kv_block)
+        z = np.where(vis, z, -np.inf)
+        n_rank = vis.sum(axis=-1)
     p = softmax_rows(z)
     C = cumulative_mass(z, p)
-    lev = assign_levels_ranked(z, fractions, num_levels, n_dense_prefix, kv_block)
+    lev = assign_levels_ranked(z, fractions, num_levels, n_dense_prefix, kv_block, n_rank)
+    if causal:
+        C, lev = apply_causal(C, lev, N, q_block, kv_block)
     return {"qbar": qbar, "kbar": kbar, "z": z, "p": p, "cmass": C, "rank": block_ranks(z), "levels": lev}
 
 
@@ -300,13 +352,14 @@ def estimate_mask_ranked(q: np.ndarray, k: np.ndarray, q_block: int, kv_block: i
 # ----------------------------------------------------------------------------
 
 def gather_keys(levels_row: np.ndarray, N: int, kv_block: int,
-                kpyr: Sequence[np.ndarray], vpyr: Sequence[np.ndarray]):
+                kpyr: Sequence[np.ndarray], vpyr: Sequence[np.ndarray], with_last: bool = False):
     """Keys, values and log pool sizes that one query block attends to.
 
     KV block j at level l contributes its pooled rows [j*b/2**l, ceil((j*b + n_j)/2**l))
-    of level l (level 0: its tokens). kpyr/vpyr: per-level [N_l, d] arrays."""
+    of level l (level 0: its tokens). kpyr/vpyr: per-level [N_l, d] arrays.
+    with_last: also return the last token each key averages (for causal masking)."""
     n_kv = block_sizes(N, kv_block)
-    ks, vs, lc = [], [], []
+    ks, vs, lc, last = [], [], [], []
     for j, l in enumerate(levels_row):
         l = int(l)
         if l < 0:
@@ -317,35 +370,49 @@ def gather_keys(levels_row: np.ndarray, N: int, kv_block: int,
         ks.append(kpyr[l][lo:hi])
         vs.append(vpyr[l][lo:hi])
         lc.append(np.log(pool_counts(N, l)[lo:hi].astype(np.float64)))
+        last.append(np.minimum((np.arange(lo, hi) + 1) * P, N) - 1)
     d = kpyr[0].shape[-1]
     if not ks:
-        return np.zeros((0, d)), np.zeros((0, d)), np.zeros(0)
-    return np.concatenate(ks), np.concatenate(vs), np.concatenate(lc)
+        out = (np.zeros((0, d)), np.zeros((0, d)), np.zeros(0))
+        return out + (np.zeros(0, dtype=np.int64),) if with_last else out
+    out = (np.concatenate(ks), np.concatenate(vs), np.concatenate(lc))
+    return out + (np.concatenate(last),) if with_last else out
 
 
 def attention_rows(qrows: np.ndarray, keys: np.ndarray, vals: np.ndarray, logc: np.ndarray,
-                   scale: float) -> Tuple[np.ndarray, np.ndarray]:
+                   scale: float, allowed: np.ndarray = None) -> Tuple[np.ndarray, np.ndarray]:
     """One softmax over mixed-resolution keys; logit = scale*<q, key> + ln(pool count).
 
-    Two passes (max, then exp and sums). Returns (O [m, d], LSE [m]); a row with no
-    key gives O = 0 and LSE = -inf."""
+    Two passes (max, then exp and sums). allowed [m, keys] (optional): False drops that
+    key for that row. Returns (O [m, d], LSE [m]); a row with no key gives O = 0 and
+    LSE = -inf."""
     m = qrows.shape[0]
     if keys.shape[0] == 0:
         return np.zeros((m, qrows.shape[1])), np.full(m, -np.inf)
     a = scale * (qrows @ keys.T) + logc[None, :]
+    if allowed is not None:
+        a = np.where(allowed, a, -np.inf)
     M = a.max(axis=1, keepdims=True)
+    empty = ~np.isfinite(M[:, 0])
+    M = np.where(np.isfinite(M), M, 0.0)
     e = np.exp(a - M)
     s = e.sum(axis=1, keepdims=True)
-    return (e @ vals) / s, (M + np.log(s))[:, 0]
+    O = (e @ vals) / np.where(s > 0, s, 1.0)
+    LSE = (M + np.log(np.where(s > 0, s, 1.0)))[:, 0]
+    O[empty] = 0.0
+    LSE[empty] = -np.inf
+    return O, LSE
 
 
 def pyramid_attention(q: np.ndarray, kpyr_levels: Sequence[np.ndarray], vpyr_levels: Sequence[np.ndarray],
                       level_map: np.ndarray, q_block: int, kv_block: int, scale: float,
-                      items=None) -> Tuple[np.ndarray, np.ndarray]:
+                      items=None, causal: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """Pyramid attention for all (or some) query blocks.
 
     q [B,H,N,d]; kpyr_levels[l] [B,H_kv,N_l,d] (level 0 = K); level_map [B,H,nqb,nkb].
     ``items``: optional iterable of (b, h, i) query blocks; other rows of the result are NaN.
+    causal: query row r sees a key only if every token it averages is at or before r
+    (for level 0: token t <= r).
     Returns O [B,H,N,d] and LSE [B,H,N] (float64)."""
     q = np.asarray(q, dtype=np.float64)
     B, H, N, d = q.shape
@@ -357,15 +424,18 @@ def pyramid_attention(q: np.ndarray, kpyr_levels: Sequence[np.ndarray], vpyr_lev
         items = [(b, h, i) for b in range(B) for h in range(H) for i in range(nqb)]
     for (b, h, i) in items:
         g = kv_head_of(h, H, H_kv)
-        keys, vals, logc = gather_keys(level_map[b, h, i], N, kv_block,
-                                       [lv[b, g] for lv in kpyr_levels], [lv[b, g] for lv in vpyr_levels])
+        keys, vals, logc, last = gather_keys(level_map[b, h, i], N, kv_block, [lv[b, g] for lv in kpyr_levels],
+                                             [lv[b, g] for lv in vpyr_levels], with_last=True)
         r0, r1 = i * q_block, min((i + 1) * q_block, N)
-        O[b, h, r0:r1], LSE[b, h, r0:r1] = attention_rows(q[b, h, r0:r1], keys, vals, logc, scale)
+        allowed = last[None, :] <= np.arange(r0, r1)[:, None] if causal else None
+        O[b, h, r0:r1], LSE[b, h, r0:r1] = attention_rows(q[b, h, r0:r1], keys, vals, logc, scale, allowed)
     return O, LSE
 
 
-def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """Textbook softmax(scale * Q K^T) V per head (KV head g(h) for query head h)."""
+def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                    causal: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Textbook softmax(scale * Q K^T) V per head (KV head g(h) for query head h);
+    causal: row r sees tokens 0..r only."""
     q = np.asarray(q, dtype=np.float64)
     B, H, N, d = q.shape
     H_kv = k.shape[1]
@@ -374,8 +444,9 @@ def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -
     for b in range(B):
         for h in range(H):
             g = kv_head_of(h, H, H_kv)
+            allowed = np.tril(np.ones((N, N), dtype=bool)) if causal else None
             O[b, h], LSE[b, h] = attention_rows(q[b, h], np.asarray(k[b, g], np.float64),
-                                                np.asarray(v[b, g], np.float64), np.zeros(N), scale)
+                                                np.asarray(v[b, g], np.float64), np.zeros(N), scale, allowed)
     return O, LSE
 
 
@@ -383,23 +454,36 @@ def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -
 # Work accounting
 # ----------------------------------------------------------------------------
 
-def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, d: int) -> float:
+def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, d: int,
+                    causal: bool = False) -> float:
     """sum over retained (b,h,i,j) of 4 * m_i * ceil(n_j / 2**l) * d: QK^T and PV on the
-    pooled rows actually attended to (no padding, no exp)."""
+    pooled rows actually attended to (no padding, no exp). Causal: only the (query row,
+    pooled row) pairs the causal rule lets through are counted."""
     m = block_sizes(N, q_block).astype(np.float64)
     n = block_sizes(N, kv_block)
     lm = level_map.reshape(-1, level_map.shape[-2], level_map.shape[-1])
     total = 0.0
     top = int(lm.max()) if lm.size else -1
     for l in range(top + 1):
-        rows_l = (-(-n // (1 << l))).astype(np.float64)          # pooled rows of each block at level l
         sel = (lm == l).astype(np.float64)                       # [B*H, nqb, nkb]
-        total += float(np.einsum("xij,i,j->", sel, m, rows_l))
+        if not causal:
+            rows_l = (-(-n // (1 << l))).astype(np.float64)      # pooled rows of each block at level l
+            total += float(np.einsum("xij,i,j->", sel, m, rows_l))
+            continue
+        P = 1 << l
+        pairs = np.zeros((len(m), len(n)))                       # visible (row, pooled row) pairs
+        for i in range(len(m)):
+            rows = np.arange(i * q_block, i * q_block + int(m[i]))
+            for j in range(len(n)):
+                lo, hi = (j * kv_block) // P, -(-(j * kv_block + int(n[j])) // P)
+                last = np.minimum((np.arange(lo, hi) + 1) * P, N) - 1
+                pairs[i, j] = float((last[None, :] <= rows[:, None]).sum())
+        total += float(np.einsum("xij,ij->", sel, pairs))
     return 4.0 * d * total
 
 
 def run_forward(q, k, v, q_block, kv_block, thresholds, num_levels, scale, io_dtype,
-                n_dense_prefix=0, items=None, ranked_fractions=None):
+                n_dense_prefix=0, items=None, ranked_fractions=None, causal=False):
     """All three steps chained: pyramid (rounded to the I/O dtype), mask, attention.
     With ranked_fractions the mask takes the ranked rule instead of the thresholds."""
     kp = build_pyramid(k, num_levels)
@@ -407,8 +491,9 @@ def run_forward(q, k, v, q_block, kv_block, thresholds, num_levels, scale, io_dt
     kp_io = [np.asarray(k, np.float64)] + [round_to_io(x, io_dtype) for x in kp[1:]]
     vp_io = [np.asarray(v, np.float64)] + [round_to_io(x, io_dtype) for x in vp[1:]]
     if ranked_fractions is None:
-        mask = estimate_mask(q, k, q_block, kv_block, thresholds, num_levels, scale, n_dense_prefix)
+        mask = estimate_mask(q, k, q_block, kv_block, thresholds, num_levels, scale, n_dense_prefix, causal)
     else:
-        mask = estimate_mask_ranked(q, k, q_block, kv_block, ranked_fractions, num_levels, scale, n_dense_prefix)
-    O, LSE = pyramid_attention(q, kp_io, vp_io, mask["levels"], q_block, kv_block, scale, items)
+        mask = estimate_mask_ranked(q, k, q_block, kv_block, ranked_fractions, num_levels, scale, n_dense_prefix,
+                                    causal)
+    O, LSE = pyramid_attention(q, kp_io, vp_io, mask["levels"], q_block, kv_block, scale, items, causal)
     return {"kpyr": kp_io, "vpyr": vp_io, "mask": mask, "O": O, "LSE": LSE}

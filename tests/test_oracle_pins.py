@@ -321,6 +321,114 @@ def test_ranked_dense_prefix_forced_after_ranking():
     np.testing.assert_array_equal(forced["rank"], plain["rank"])
 
 
+# ----------------------------------------------------------------------------- causal use
+
+def test_causal_blocks_closed_form():
+    vis, diag = o.causal_blocks(300, 128, 64)            # 3 query blocks, 5 KV blocks (last one ragged)
+    np.testing.assert_array_equal(vis, [[1, 1, 0, 0, 0], [1, 1, 1, 1, 0], [1, 1, 1, 1, 1]])
+    np.testing.assert_array_equal(diag, [[1, 1, 0, 0, 0], [0, 0, 1, 1, 0], [0, 0, 0, 0, 1]])
+    vis, diag = o.causal_blocks(256, 64, 64)
+    np.testing.assert_array_equal(vis, np.tril(np.ones((4, 4), bool)))
+    np.testing.assert_array_equal(diag, np.eye(4, dtype=bool))
+
+
+def test_causal_dense_map_equals_torch_causal_sdpa():
+    q, k, v = small_case(60, N=200, d=8)
+    s = 0.4
+    O_ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True, scale=s).numpy()
+    lev = np.zeros((1, 2, 4, 4), dtype=np.int8)           # every block at level 0: the causal rule masks
+    kp, vp = o.build_pyramid(k, 4), o.build_pyramid(v, 4)
+    O, LSE = o.pyramid_attention(q, kp, vp, lev, 64, 64, s, causal=True)
+    np.testing.assert_allclose(O, O_ref, rtol=0, atol=1e-12)
+    Od, LSEd = o.dense_attention(q, k, v, s, causal=True)
+    np.testing.assert_allclose(O, Od, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(LSE, LSEd, rtol=0, atol=1e-12)
+    # row 0 sees only token 0
+    np.testing.assert_allclose(O[0, :, 0], v[0, :, 0], rtol=0, atol=1e-15)
+
+
+def test_causal_row_equals_attention_on_truncated_sequence():
+    # With the causal mask's map (blocks reaching the query block at level 0, earlier blocks
+    # pooled or pruned), row r is pyramid attention over the first r+1 tokens only.
+    N, d, bq = 333, 8, 128
+    q, k, v = small_case(61, N=N, d=d)
+    s = 0.35
+    m = o.estimate_mask(q, k, bq, 64, (0.3, 0.5, 0.7, 0.8), 4, s, causal=True)
+    lev = m["levels"]
+    O, LSE = o.pyramid_attention(q, o.build_pyramid(k, 4), o.build_pyramid(v, 4), lev, bq, 64, s, causal=True)
+    for r in (0, 5, 63, 64, 127, 128, 200, 255, 256, 300, 332):
+        i = r // bq
+        kt, vt = k[:, :, :r + 1], v[:, :, :r + 1]
+        nkb_t = -(-(r + 1) // 64)
+        lev_t = np.full((1, 2, 1, nkb_t), -1, dtype=np.int8)
+        lev_t[..., 0, :] = lev[:, :, i, :nkb_t]
+        qt = np.zeros((1, 2, r + 1, d))
+        qt[:, :, r] = q[:, :, r]
+        Ot, LSEt = o.pyramid_attention(qt, o.build_pyramid(kt, 4), o.build_pyramid(vt, 4), lev_t, r + 1, 64, s)
+        np.testing.assert_allclose(O[:, :, r], Ot[:, :, r], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(LSE[:, :, r], LSEt[:, :, r], rtol=0, atol=1e-12)
+
+
+def test_causal_pooled_key_needs_all_its_tokens():
+    # A pooled key is visible to row r only when every token it averages is <= r.
+    N, d = 128, 4
+    q, k, v = small_case(62, H=1, Hkv=1, N=N, d=d)
+    lev = np.array([[[[0, -1], [0, 2]]]], dtype=np.int8)   # q-block 1 sees block 1 at level 2
+    kp, vp = o.build_pyramid(k, 3), o.build_pyramid(v, 3)
+    O, LSE = o.pyramid_attention(q, kp, vp, lev, 64, 64, 0.5, causal=True)
+    for r in (64, 66, 67, 70, 127):
+        keys = [k[0, 0, t] for t in range(64)]
+        vals = [v[0, 0, t] for t in range(64)]
+        wl = [0.0] * 64
+        for p in range(16, 32):                            # level-2 rows of block 1: tokens 4p..4p+3
+            if 4 * p + 3 <= r:
+                keys.append(kp[2][0, 0, p])
+                vals.append(vp[2][0, 0, p])
+                wl.append(math.log(4))
+        o_ref, lse_ref = brute_attention_row(q[0, 0, r], keys, vals, wl, 0.5)
+        np.testing.assert_allclose(O[0, 0, r], o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(LSE[0, 0, r], lse_ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("rule", ["threshold", "ranked"])
+def test_causal_mask_equals_mask_of_truncated_problem(rule):
+    # The causal mask row of query block i is the non-causal mask of the problem cut after
+    # the last KV block that block can see, with the blocks reaching its rows set to level 0.
+    N, d, bq = 700, 8, 128
+    q = rng(63).standard_normal((1, 2, N, d))
+    k = rng(64).standard_normal((1, 2, N, d))
+    s, tau, fr = 0.45, (0.25, 0.5, 0.7, 0.85), (0.1, 0.3, 0.5, 0.7)
+    if rule == "threshold":
+        m = o.estimate_mask(q, k, bq, 64, tau, 4, s, causal=True)
+    else:
+        m = o.estimate_mask_ranked(q, k, bq, 64, fr, 4, s, causal=True)
+    vis, diag = o.causal_blocks(N, bq, 64)
+    assert np.all(m["levels"][..., ~vis] == -1) and np.all(m["levels"][..., diag] == 0)
+    assert np.all(m["cmass"][..., ~vis] == 1.0)
+    np.testing.assert_allclose(m["p"].sum(-1), 1.0, rtol=0, atol=1e-12)
+    for i in range(vis.shape[0]):
+        nv = int(vis[i].sum())
+        Nt = min(N, 64 * nv)
+        if rule == "threshold":
+            t = o.estimate_mask(q[:, :, :Nt], k[:, :, :Nt], bq, 64, tau, 4, s)
+        else:
+            t = o.estimate_mask_ranked(q[:, :, :Nt], k[:, :, :Nt], bq, 64, fr, 4, s)
+        np.testing.assert_allclose(m["cmass"][:, :, i, :nv], t["cmass"][:, :, i], rtol=0, atol=1e-13)
+        expect = t["levels"][:, :, i].copy()
+        expect[..., diag[i, :nv]] = 0
+        np.testing.assert_array_equal(m["levels"][:, :, i, :nv], expect)
+
+
+def test_causal_effective_flops_closed_form():
+    N, d = 300, 8
+    lev = np.zeros((1, 1, 3, 5), dtype=np.int8)
+    assert o.effective_flops(lev, N, 128, 64, d, causal=True) == 4 * d * N * (N + 1) / 2
+    lev2 = o.estimate_mask(rng(65).standard_normal((1, 1, N, d)), rng(66).standard_normal((1, 1, N, d)),
+                           128, 64, (0.2, 0.4, 0.6, 0.8), 4, 0.5, causal=True)["levels"]
+    assert o.effective_flops(lev2, N, 128, 64, d, causal=True) < o.effective_flops(lev2, N, 128, 64, d)
+
+
 # ----------------------------------------------------------------------------- attention (O6)
 
 def brute_attention_row(qr, keys, vals, weights_log, scale):
