@@ -50,17 +50,31 @@ def attention_kernel_name(d: int, q_block: int, dtype: str) -> str:
     return f"pyramid_attn_fwd_kernel<{t},{d},{q_block // 32}>"
 
 
-def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, d: int) -> float:
-    """sum over retained (b,h,i,j): 4 * m_i * ceil(n_j / 2^l) * d."""
+def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, d: int,
+                    causal: bool = False) -> float:
+    """sum over retained (b,h,i,j): 4 * d * (query row, pooled row) pairs, i.e.
+    4 * m_i * ceil(n_j / 2^l) * d; in causal use only the pairs where the pooled row's last
+    token is at or before the query row count."""
     nqb, nkb = level_map.shape[-2], level_map.shape[-1]
-    m = np.minimum(q_block, N - np.arange(nqb) * q_block).astype(np.float64)
+    m = np.minimum(q_block, N - np.arange(nqb) * q_block).astype(np.int64)
     n = np.minimum(kv_block, N - np.arange(nkb) * kv_block)
     lm = level_map.reshape(-1, nqb, nkb)
     total = 0.0
     for l in range(4):
-        rows = (-(-n // (1 << l))).astype(np.float64)
         sel = (lm == l).astype(np.float64)
-        total += float(np.einsum("xij,i,j->", sel, m, rows))
+        if not sel.any():
+            continue
+        if not causal:
+            rows = (-(-n // (1 << l))).astype(np.float64)
+            total += float(np.einsum("xij,i,j->", sel, m.astype(np.float64), rows))
+            continue
+        P = 1 << l
+        p = np.arange(kv_block // P)
+        last = np.minimum(np.arange(nkb)[:, None] * kv_block + (p[None, :] + 1) * P, N) - 1
+        last = np.where(p[None, :] * P < n[:, None], last, 1 << 40)
+        r0 = (np.arange(nqb) * q_block)[:, None, None]
+        pairs = np.clip(r0 + m[:, None, None] - np.maximum(r0, last[None]), 0, None).sum(-1).astype(np.float64)
+        total += float(np.einsum("xij,ij->", sel, pairs))
     return 4.0 * d * total
 
 
@@ -99,9 +113,9 @@ def cpu_baseline(w, q, k, v, tau, fractions=None):
     kh = k[:, :nkv].astype(np.float64)
     vh = v[:, :nkv].astype(np.float64)
     res = o.run_forward(qh, kh, vh, w.q_block, w.kv_block, tau, w.num_levels, w.scale, w.dtype,
-                        w.n_dense_prefix, ranked_fractions=fractions)
+                        w.n_dense_prefix, ranked_fractions=fractions, causal=w.causal)
     dt = time.perf_counter() - t0
-    fl = o.effective_flops(res["mask"]["levels"], w.N, w.q_block, w.kv_block, w.d)
+    fl = o.effective_flops(res["mask"]["levels"], w.N, w.q_block, w.kv_block, w.d, causal=w.causal)
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{w.name}: all three steps (pyramid, mask, attention) for heads 0..{nh - 1} of {w.H}, "
@@ -115,6 +129,8 @@ def compare_rules(psa, w, qd, kd, vd, steps: int):
     allow. Every step runs in the library's kernels; dense attention is the same attention
     kernel with every block at level 0. Prints one JSON line."""
     import torch
+    if w.causal:
+        raise SystemExit("--compare-rules covers bidirectional workloads only")
     dev = qd.device
     tau, fr = w.thresholds(), list(w.ranked_fractions())
 
@@ -222,7 +238,7 @@ def main():
         compare_rules(psa, w, qd, kd, vd, args.steps)
         return
     prob = psa.Problem(B=w.B, H=w.H, H_kv=w.H_kv, N=w.N, d=w.d, q_block=w.q_block, kv_block=w.kv_block,
-                       num_levels=w.num_levels, dtype=w.dtype)
+                       num_levels=w.num_levels, dtype=w.dtype, causal=w.causal)
     R = prob.pyramid_rows
     k_pyr = torch.empty((w.B, w.H_kv, R, w.d), dtype=dt, device=dev)
     v_pyr = torch.empty_like(k_pyr)
@@ -260,7 +276,7 @@ def main():
     pyr_ms, mask_ms, attn_ms = (float(np.mean(per[:, i])) for i in range(3))
 
     lm = level_map.cpu().numpy()
-    flops = effective_flops(lm, w.N, w.q_block, w.kv_block, w.d)
+    flops = effective_flops(lm, w.N, w.q_block, w.kv_block, w.d, causal=w.causal)
     rho = flops / w.dense_flops()
     esz = 2 if w.dtype == "bf16" else 4
     kv_bytes = 2 * w.B * w.H_kv * w.N * w.d * esz
@@ -279,7 +295,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "B": w.B, "H": w.H, "H_kv": w.H_kv,
                    "N": w.N, "d": w.d, "q_block": w.q_block, "kv_block": w.kv_block,
-                   "num_levels": w.num_levels, "parallelism": "single GPU",
+                   "num_levels": w.num_levels, "causal": w.causal, "parallelism": "single GPU",
                    **({"rule": "threshold", "thresholds": list(tau)} if fractions is None
                       else {"rule": "ranked", "fractions": fractions})},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,

@@ -39,6 +39,16 @@
  *    attention multiplies bf16 operands on the matrix cores with float32
  *    accumulation and a float32 online softmax. float32 I/O is rounded to bf16
  *    on its way into the matrix cores.
+ *
+ * Causal use (PSA serves causal attention for generation and bidirectional attention
+ * for understanding: top168.com article, paragraph on causal and bidirectional use):
+ *  - mask: query block i (rows r0..r1-1) ranks only the KV blocks that hold a token
+ *    at or before r1-1 (softmax, C and the ranked counts over those blocks); blocks
+ *    that hold a token at or after r0 are then set to level 0 (a pooled key would
+ *    mix in tokens later than some of the block's rows); later blocks are -1 and
+ *    report C = 1 (also when n_dense_prefix covers them);
+ *  - attention: row r sees a key only if every token it averages is at or before r
+ *    (at level 0: token t <= r), whatever the level map says.
  */
 #ifndef PSA_H_
 #define PSA_H_
@@ -71,6 +81,8 @@ typedef struct {
   int32_t num_levels;         /* L in [1, 4]: level l pools 2^l tokens                 */
   psa_dtype_t dtype;          /* I/O dtype of q, k, v, k_pyr, v_pyr, o                 */
   float scale;                /* softmax scale; <= 0 selects 1/sqrt(d)                 */
+  int32_t causal;             /* 0: bidirectional; 1: causal (query row r sees tokens
+                                 0..r; rules under "Causal use" above)                 */
 } psa_problem_t;
 
 /* Rows of the concatenated pyramid: sum over l = 1..L-1 of ceil(N / 2^l).
@@ -129,10 +141,13 @@ psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const f
  * pooled levels (skillmd.com page, "Level assignment", whose keep ratio is
  * fractions[0]). With num_levels == 1 it is the binary top-k block-sparse mask.
  * Scores and ranking are those of psa_estimate_mask. With K_l = floor(fractions[l]
- * * nkb) (the product in double precision), the block of rank r (0 = most
- * important) gets level_ij = min{l : r < K_l}, or -1 (pruned) if there is none.
+ * * n) (the product in double precision; n = nkb, or under causal use the row's
+ * visible blocks), the block of rank r (0 = most important) gets
+ * level_ij = min{l : r < K_l}, or -1 (pruned) if there is none.
  * So each row has K_l - K_{l-1} blocks at level l (K_{-1} = 0) before the dense
- * prefix is applied as in psa_estimate_mask. cmass_out (nullable): C as defined there.
+ * prefix (and, under causal use, the level-0 rule for blocks reaching the query
+ * block's rows) is applied as in psa_estimate_mask. cmass_out (nullable): C as
+ * defined there.
  * fractions: host array of num_levels doubles, nondecreasing, each in [0, 1].
  * Workspace, supported sizes and errors as psa_estimate_mask.
  */

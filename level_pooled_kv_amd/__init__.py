@@ -41,7 +41,7 @@ class psa_problem_t(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("H_kv", ctypes.c_int32),
         ("N", ctypes.c_int32), ("d", ctypes.c_int32),
         ("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32), ("num_levels", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
     ]
 
 
@@ -89,11 +89,12 @@ class Problem:
     num_levels: int = 4
     dtype: str = "bf16"           # "bf16" or "f32"
     scale: float = 0.0            # <= 0 selects 1/sqrt(d)
+    causal: bool = False          # query row r sees tokens 0..r only
 
     def c(self) -> psa_problem_t:
         return psa_problem_t(self.B, self.H, self.H_kv, self.N, self.d, self.q_block, self.kv_block,
                              self.num_levels, PSA_BF16 if self.dtype == "bf16" else PSA_F32,
-                             float(self.scale))
+                             float(self.scale), int(self.causal))
 
     @property
     def torch_dtype(self):

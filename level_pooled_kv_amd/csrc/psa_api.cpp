@@ -42,6 +42,8 @@ psa_status_t check_problem(const psa_problem_t* p) {
     return fail(PSA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)p->dtype);
   if (isnan(p->scale) || isinf(p->scale))
     return fail(PSA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (p->causal != 0 && p->causal != 1)
+    return fail(PSA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", p->causal);
   if (p->d != 64 && p->d != 128)
     return fail(PSA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", p->d);
   if (p->q_block != 64 && p->q_block != 128)
@@ -152,11 +154,11 @@ psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const v
 }
 
 // Checks shared by both mask entry points, then the launch. Exactly one of tau and
-// counts is non-NULL: the threshold rule or the ranked rule.
+// fractions is non-NULL: the threshold rule or the ranked rule.
 static psa_status_t estimate_mask_common(const psa_problem_t* prob, const void* q, const float* k_bar,
                                          int32_t n_dense_prefix, int8_t* level_map, float* cmass_out,
                                          void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                         const float* tau, const int* counts, const char* what) {
+                                         const float* tau, const double* fractions, const char* what) {
   REQUIRE_PTR(q, "q");
   REQUIRE_PTR(k_bar, "k_bar");
   REQUIRE_PTR(level_map, "level_map");
@@ -180,10 +182,11 @@ static psa_status_t estimate_mask_common(const psa_problem_t* prob, const void* 
   a.n_dense_prefix = n_dense_prefix;
   a.bf16 = prob->dtype == PSA_BF16;
   a.scale = effective_scale(prob);
-  a.ranked = counts != nullptr;
+  a.ranked = fractions != nullptr;
+  a.causal = prob->causal != 0;
   for (int l = 0; l < psa::kMaxLevels; ++l) {
     a.tau[l] = tau && l < prob->num_levels ? tau[l] : 0.f;
-    a.rank_count[l] = counts && l < prob->num_levels ? counts[l] : 0;
+    a.frac[l] = fractions && l < prob->num_levels ? fractions[l] : 0.0;
   }
   return hip_status(psa::launch_mask(a, stream), what);
 }
@@ -216,8 +219,6 @@ psa_status_t psa_estimate_mask_ranked(const psa_problem_t* prob, const void* q, 
   psa_status_t s = check_problem(prob);
   if (s != PSA_OK) return s;
   if (!fractions) return fail(PSA_ERR_INVALID_ARGUMENT, "fractions is NULL");
-  const int64_t nkb = ceil_div(prob->N, psa::kKvBlock);
-  int counts[psa::kMaxLevels] = {0, 0, 0, 0};
   for (int l = 0; l < prob->num_levels; ++l) {
     const double f = fractions[l];
     if (!(f >= 0.0 && f <= 1.0))
@@ -225,10 +226,10 @@ psa_status_t psa_estimate_mask_ranked(const psa_problem_t* prob, const void* q, 
     if (l > 0 && f < fractions[l - 1])
       return fail(PSA_ERR_INVALID_ARGUMENT, "fractions must be nondecreasing (fractions[%d] < fractions[%d])",
                   l, l - 1);
-    counts[l] = (int)floor(f * (double)nkb);   // in [0, nkb]
   }
+  // the kernel takes K_l = floor(f_l * n) per row (n = nkb, or the row's visible blocks)
   return estimate_mask_common(prob, q, k_bar, n_dense_prefix, level_map, cmass_out, workspace, workspace_bytes,
-                              stream, nullptr, counts, "psa_estimate_mask_ranked launch");
+                              stream, nullptr, fractions, "psa_estimate_mask_ranked launch");
 }
 
 psa_status_t psa_attention_fwd(const psa_problem_t* prob, const void* q, const void* k, const void* v,
@@ -257,6 +258,7 @@ psa_status_t psa_attention_fwd(const psa_problem_t* prob, const void* q, const v
   a.nkb = (int)ceil_div(prob->N, psa::kKvBlock);
   a.L = prob->num_levels;
   a.bf16 = prob->dtype == PSA_BF16;
+  a.causal = prob->causal != 0;
   a.scale = effective_scale(prob);
   a.pyr_rows = pyramid_rows(prob);
   level_offsets(prob, a.off, a.rows);

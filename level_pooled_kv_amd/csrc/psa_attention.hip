@@ -47,7 +47,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
                         const T* __restrict__ kp, const T* __restrict__ vp,
                         const int8_t* __restrict__ level_map, T* __restrict__ o, float* __restrict__ lse,
                         int H, int H_kv, int N, int nqb, int nkb, int L, int total_items, int per_xcd,
-                        int64_t pyr_rows, int rows1, int rows2, float cs /* scale * log2(e) */) {
+                        int64_t pyr_rows, int rows1, int rows2, float cs /* scale * log2(e) */, int causal) {
   using C = AttnCfg<D, NW>;
   constexpr int CPR = C::kCpr, RPB = C::kRpb, BPW = C::kBpw;
   constexpr bool kDirect = sizeof(T) == 2;     // bf16: global -> LDS without registers
@@ -57,6 +57,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   __shared__ __align__(16) uint16_t K0[64 * D], K1[64 * D];
   __shared__ __align__(16) uint16_t V0[64 * D], V1[64 * D];
   __shared__ float corr[2][64];
+  __shared__ int ltok[2][64];                    // diagonal tiles: last token of each staged key row
   __shared__ int16_t blist[kMaxKvBlocks];
   __shared__ uint32_t tdesc[kMaxKvBlocks + 4];   // per tile: level | list base << 2 | segs << 16 | irregular << 31
   __shared__ int s_tile[5];
@@ -71,11 +72,11 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 
   // ---- compact the level-map row into level-major block lists (wave 0)
   const int8_t* lrow = level_map + (int64_t)item * nkb;   // item == (b*H + h)*nqb + qi
-  if (wave == 0) build_tile_lists(lrow, nkb, L, N, blist, tdesc, s_tile);
+  const int q0 = qi * (32 * NW);
+  if (wave == 0) build_tile_lists(lrow, nkb, L, N, causal ? q0 / 64 : nkb, blist, tdesc, s_tile);
 
   // ---- Q operand in registers: lane (row = lane%32, half = lane/32) holds d = 16c + 8*half + 0..7
   const int half = lane >> 5, l32 = lane & 31;
-  const int q0 = qi * (32 * NW);
   const int my_row = q0 + 32 * wave + l32;
   bf16x8 qreg[C::kQc];
   {
@@ -149,6 +150,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         fv[i].load(reinterpret_cast<const float*>(vb + voff));
       }
       if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
+      if (ti.diag && st_pchunk == 0) ltok[buf][row] = key_last_token(ok, lvl, prow, N);
     }
   };
   // Direct-load path: the byte offsets of tile t's staged rows are computed up front
@@ -178,6 +180,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       st.koff[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ k_swz<D>(row))) * (int)sizeof(T));
       st.voff[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ v_swz<D>(row))) * (int)sizeof(T));
       if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
+      if (ti.diag && st_pchunk == 0) ltok[buf][row] = key_last_token(ok, lvl, prow, N);
     }
     return st;
   };
@@ -262,6 +265,13 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         for (int x = 0; x < 16; ++x)
           sacc[kb][x] += corr[buf][32 * kb + 8 * (x >> 2) + 4 * half + (x & 3)];
     }
+    if (ti.diag) {   // causal: a key is seen only by rows at or after its last token
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+          if (ltok[buf][32 * kb + 8 * (x >> 2) + 4 * half + (x & 3)] > my_row) sacc[kb][x] = -INFINITY;
+    }
 
     // online softmax (base 2); this tile's keys all carry bias lvl
     float tmax = sacc[0][0];
@@ -277,16 +287,17 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const float mt = fmaf(tmax, cs, lvlf);
     const bool upd = mt > m_run + 8.0f;
     if (__ballot(upd)) {
-      const float m_new = upd ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // lanes that keep their max scale by 1 (also when it is still -inf after causal masking)
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int tt = 0; tt < C::kDt; ++tt)
 #pragma unroll
         for (int x = 0; x < 16; ++x) oacc[tt][x] *= alpha;
-      m_run = m_new;
+      m_run = upd ? mt : m_run;
     }
-    const float moff = lvlf - m_run;
+    // a row that has seen no key yet (possible only after causal masking) keeps p = 0
+    const float moff = ti.diag && m_run == -INFINITY ? 0.f : lvlf - m_run;
     bf16x8 preg[4];
     float lsum = 0.f;
 #pragma unroll
@@ -366,7 +377,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                      static_cast<const T*>(a.k_pyr), static_cast<const T*>(a.v_pyr), a.level_map,
                      static_cast<T*>(a.o), a.lse, a.H, a.H_kv, a.N, a.nqb, a.nkb, a.L, total, per,
-                     a.pyr_rows, a.rows[1], a.rows[2], cs);
+                     a.pyr_rows, a.rows[1], a.rows[2], cs, a.causal ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// Pieces shared by the two gfx950 attention kernels of the PSA forward path: LDS tile
+// Pieces of the gfx950 attention kernel of the PSA forward path: LDS tile
 // layout, staging geometry and the per-query-block tile lists.
 #pragma once
 
@@ -58,10 +58,11 @@ __host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4
 
 
 // Per-tile descriptor (built once per query block): level | first block-list index << 2 |
-// valid segments << 16 | irregular << 31.
-struct TileInfo { int lvl, base, nseg; bool irr; };
+// valid segments << 16 | causal-diagonal << 30 | irregular << 31.
+struct TileInfo { int lvl, base, nseg; bool diag, irr; };
 __device__ __forceinline__ TileInfo decode_tile(uint32_t d) {
-  return TileInfo{(int)(d & 3u), (int)((d >> 2) & 0x3fffu), (int)((d >> 16) & 15u), (d >> 31) != 0};
+  return TileInfo{(int)(d & 3u), (int)((d >> 2) & 0x3fffu), (int)((d >> 16) & 15u), ((d >> 30) & 1u) != 0,
+                  (d >> 31) != 0};
 }
 
 // Wave-level (call from one whole wave): compact one level-map row into level-major
@@ -70,8 +71,12 @@ __device__ __forceinline__ TileInfo decode_tile(uint32_t d) {
 // A hardware tile is 64 key rows of ONE level: 1 block at level 0, 2 at level 1,
 // 4 at level 2, 8 at level 3. A tile is irregular (needs per-key fixups) when it is
 // the last of its level and has padding segments or holds the ragged final KV block.
+// Under causal use a tile is diagonal (needs per-query masking) when its last block
+// index is diag_from or more (the blocks reaching the query block's own rows; pass
+// nkb for none).
 __device__ __forceinline__ void build_tile_lists(const int8_t* __restrict__ lrow, int nkb, int L, int N,
-                                                 int16_t* blist, uint32_t* tdesc, int* s_tile) {
+                                                 int diag_from, int16_t* blist, uint32_t* tdesc,
+                                                 int* s_tile) {
   const int lane = threadIdx.x & 63;
   int cnt[4] = {0, 0, 0, 0};
   for (int j0 = 0; j0 < nkb; j0 += 64) {
@@ -117,10 +122,17 @@ __device__ __forceinline__ void build_tile_lists(const int8_t* __restrict__ lrow
     for (int u = lane; u < ntl; u += 64) {
       const int nseg = min(1 << l, cnt[l] - (u << l));
       const bool irr = u == ntl - 1 && (nseg < (1 << l) || tail);
+      const bool diag = blist[start[l] + (u << l) + nseg - 1] >= diag_from;
       tdesc[tfirst[l] + u] = (uint32_t)l | ((uint32_t)(start[l] + (u << l)) << 2) | ((uint32_t)nseg << 16) |
-                             (irr ? 0x80000000u : 0u);
+                             (diag ? 0x40000000u : 0u) | (irr ? 0x80000000u : 0u);
     }
   }
+}
+
+// Last token a staged key row averages (for causal masking of diagonal tiles); padding
+// rows and rows past the sequence get INT_MAX, so every query masks them.
+__device__ __forceinline__ int key_last_token(bool ok, int lvl, int prow, int N) {
+  return ok ? min((prow + 1) << lvl, N) - 1 : 0x7fffffff;
 }
 
 // Logit correction of one staged key row of an irregular tile, in units of the raw dot

@@ -27,15 +27,20 @@ struct MaskArgs {
   bool bf16;
   float scale;
   float tau[kMaxLevels];
-  bool ranked;                   // level by rank: rank < rank_count[l] instead of C < tau[l]
-  int rank_count[kMaxLevels];    // cumulative block counts of the ranked rule (0 past L)
+  bool ranked;                   // level by rank: rank < floor(frac[l] * visible blocks) instead of C < tau[l]
+  double frac[kMaxLevels];       // cumulative block fractions of the ranked rule
+  bool causal;                   // rank only the blocks a query block can see (see psa.h)
 };
+
+// Kernel argument: the ranked rule's cumulative fractions (double, as the host gives them).
+struct RankFractions { double f[kMaxLevels]; };
 
 struct AttnArgs {
   const void* q; const void* k; const void* v; const void* k_pyr; const void* v_pyr;
   const int8_t* level_map; void* o; float* lse;
   int B, H, H_kv, N, d, q_block, nqb, nkb, L;
   bool bf16;
+  bool causal;                   // row r sees a pooled key only if all its tokens are <= r
   float scale;
   int64_t pyr_rows;
   int off[kMaxLevels];           // row offset of level l (l >= 1) in the pyramid

@@ -330,11 +330,21 @@ template <int E, bool RANKED>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
                    int N, int nkb, int nrows, int L, int n_dense_prefix,
-                   float tau0, float tau1, float tau2, float tau3, int4 kcut) {
+                   float tau0, float tau1, float tau2, float tau3, RankFractions frac,
+                   int q_block, int nqb, int causal) {
   constexpr int NP = 64 * E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * (kMaskThreads / 64) + wave;
   if (row >= nrows) return;                 // whole wave; no barrier in this kernel
+  // Causal use: the row ranks only the nvis blocks that hold a token at or before its
+  // query block's last row; blocks from dfirst on reach the block's own rows and stay at
+  // full resolution (a pooled key would mix in later tokens); later blocks are pruned.
+  int nvis = nkb, dfirst = nkb;
+  if (causal) {
+    const int r0 = (row % nqb) * q_block;
+    nvis = (min(N, r0 + q_block) - 1) / 64 + 1;
+    dfirst = r0 / 64;
+  }
   const float* zr = z + (int64_t)row * NP + E * lane;
   float zz[E];
   if constexpr (E >= 4) {
@@ -354,24 +364,38 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
   if (want_mass) {
 #pragma unroll
     for (int r = 0; r < E; ++r)
-      if (E * lane + r < nkb) mx = fmaxf(mx, zz[r]);
+      if (E * lane + r < nvis) mx = fmaxf(mx, zz[r]);
     mx = wave_max(mx);
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < E; ++r)
-      if (E * lane + r < nkb) s += __expf(zz[r] - mx);
+      if (E * lane + r < nvis) s += __expf(zz[r] - mx);
     s = wave_sum(s);
     inv_s = 1.0f / s;
   }
   const float tau[4] = {tau0, tau1, tau2, tau3};
-  const int K[4] = {kcut.x, kcut.y, kcut.z, kcut.w};
+  // ranked rule: K_l = floor(f_l * nvis) in double precision (the host's expression)
+  int K[4];
+#pragma unroll
+  for (int l = 0; l < 4; ++l) K[l] = RANKED && l < L ? (int)floor(frac.f[l] * (double)nvis) : 0;
   int8_t* lrow = level_map + (int64_t)row * nkb;
+  float* crow = cmass ? cmass + (int64_t)row * nkb : nullptr;
+  if (nvis < nkb) {   // causal: blocks after the query block are pruned; all the mass lies ahead
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int j = E * lane + r;
+      if (j >= nvis && j < nkb) {
+        lrow[j] = -1;
+        if (crow) crow[j] = 1.f;
+      }
+    }
+  }
 
   if (cmass == nullptr) {
     uint32_t orig[E], key[E];
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-      orig[r] = E * lane + r < nkb ? score_key(zz[r]) : kPadKey32;
+      orig[r] = E * lane + r < nvis ? score_key(zz[r]) : kPadKey32;
       key[r] = orig[r];
     }
     wave_bitonic_sort32<E>(key, lane);
@@ -417,12 +441,12 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
 #pragma unroll
       for (int r = 0; r < E; ++r) {
         const int j = E * lane + r;
-        if (j < nkb) {
+        if (j < nvis) {
           int lev = -1;
 #pragma unroll
           for (int l = kMaxLevels - 1; l >= 0; --l)
             if (l < L && cnt[l] > 0 && orig[r] <= cut[l]) lev = l;
-          if (64 * j < n_dense_prefix) lev = 0;
+          if (64 * j < n_dense_prefix || j >= dfirst) lev = 0;
           lrow[j] = (int8_t)lev;
         }
       }
@@ -435,31 +459,30 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const int j = E * lane + r;
-    key[r] = j < nkb ? rank_key(zz[r], j) : ~0ull;   // padding sorts last
+    key[r] = j < nvis ? rank_key(zz[r], j) : ~0ull;   // padding (and invisible blocks) sort last
   }
   wave_bitonic_sort<E>(key, lane);
   float p[E], tot = 0.f;
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const uint32_t j = (uint32_t)key[r];
-    p[r] = want_mass && j < (uint32_t)nkb ? __expf(key_score(key[r]) - mx) * inv_s : 0.f;
+    p[r] = want_mass && j < (uint32_t)nvis ? __expf(key_score(key[r]) - mx) * inv_s : 0.f;
     tot += p[r];
   }
   float run = want_mass ? wave_exclusive_sum(tot, lane) : 0.f;
-  float* crow = cmass ? cmass + (int64_t)row * nkb : nullptr;
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const uint32_t j = (uint32_t)key[r];
     const float C = run;
     run += p[r];
-    if (j < (uint32_t)nkb) {
+    if (j < (uint32_t)nvis) {
       int lev = -1;
 #pragma unroll
       for (int l = kMaxLevels - 1; l >= 0; --l) {
         const bool in = RANKED ? E * lane + r < K[l] : C < tau[l];   // sorted position = rank
         if (l < L && in) lev = l;
       }
-      if (64 * (int)j < n_dense_prefix) lev = 0;
+      if (64 * (int)j < n_dense_prefix || (int)j >= dfirst) lev = 0;
       lrow[j] = (int8_t)lev;
       if (crow) crow[j] = C;
     }
@@ -475,10 +498,11 @@ int mask_score_stride(int nkb) {
 
 template <int E, bool RANKED>
 static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
-  const int4 kcut = make_int4(a.rank_count[0], a.rank_count[1], a.rank_count[2], a.rank_count[3]);
+  RankFractions frac;
+  for (int l = 0; l < kMaxLevels; ++l) frac.f[l] = a.frac[l];
   hipLaunchKernelGGL((block_level_kernel<E, RANKED>), dim3((nrows + 3) / 4), dim3(kMaskThreads), 0, stream,
                      a.z, a.level_map, a.cmass, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0], a.tau[1],
-                     a.tau[2], a.tau[3], kcut);
+                     a.tau[2], a.tau[3], frac, a.q_block, a.nqb, a.causal ? 1 : 0);
 }
 
 template <int E>

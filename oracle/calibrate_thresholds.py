@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE (writes synth/thresholds.json; uses only the oracle and the
 seeded input generator).
 
-The workloads state a target FLOP fraction rho (computed FLOPs / dense FLOPs),
+The workloads state a target FLOP fraction rho (computed FLOPs / dense FLOPs; for a
+workload in causal use both count only the (query, key) pairs the causal rule lets through),
 not thresholds. Reading taken: a one-parameter family tau_l(x) = tau0_l ** x with
 tau0 = (0.6, 0.8, 0.9, 0.95) (the tiny workload's thresholds); rho is monotone
 non-increasing in x, so bisection on log x finds x with |rho - target| <= 0.005
@@ -47,17 +48,34 @@ def block_means_streamed(w: W.Workload):
     return qbar, kbar
 
 
+def threshold_levels(w: W.Workload, C: np.ndarray, tau, n_dense_prefix: int) -> np.ndarray:
+    lev = o.assign_levels(C, tau, w.num_levels, n_dense_prefix, w.kv_block)
+    if w.causal:
+        _, lev = o.apply_causal(C, lev, w.N, w.q_block, w.kv_block)
+    return lev
+
+
+def rho_of(w: W.Workload, lev: np.ndarray) -> float:
+    return o.effective_flops(lev, w.N, w.q_block, w.kv_block, w.d, causal=w.causal) / w.dense_flops()
+
+
 def rho_for(w: W.Workload, z: np.ndarray, C: np.ndarray, tau) -> float:
-    lev = o.assign_levels(C, tau, w.num_levels, w.n_dense_prefix, w.kv_block)
-    return o.effective_flops(lev, w.N, w.q_block, w.kv_block, w.d) / w.dense_flops()
+    return rho_of(w, threshold_levels(w, C, tau, w.n_dense_prefix))
+
+
+def scores(w: W.Workload):
+    """z (invisible blocks at -inf under causal use) and the cumulative mass C."""
+    qbar, kbar = block_means_streamed(w)
+    z = o.block_scores(qbar, kbar, o.block_sizes(w.N, w.kv_block), w.scale)
+    if w.causal:
+        vis, _ = o.causal_blocks(w.N, w.q_block, w.kv_block)
+        z = np.where(vis, z, -np.inf)
+    return z, o.cumulative_mass(z, o.softmax_rows(z))
 
 
 def calibrate(w: W.Workload, tol: float = 0.005):
     t0 = time.time()
-    qbar, kbar = block_means_streamed(w)
-    z = o.block_scores(qbar, kbar, o.block_sizes(w.N, w.kv_block), w.scale)
-    p = o.softmax_rows(z)
-    C = o.cumulative_mass(z, p)
+    z, C = scores(w)
 
     def tau_of(x):
         return tuple(float(np.float32(t ** x)) for t in W.TAU0[: w.num_levels])
@@ -85,9 +103,9 @@ def calibrate(w: W.Workload, tol: float = 0.005):
 
 def match_ranked(w: W.Workload, entry: dict) -> dict:
     t0 = time.time()
-    qbar, kbar = block_means_streamed(w)
-    z = o.block_scores(qbar, kbar, o.block_sizes(w.N, w.kv_block), w.scale)
-    C = o.cumulative_mass(z, o.softmax_rows(z))
+    if w.causal:
+        raise ValueError("ranked fractions are matched for bidirectional workloads only")
+    z, C = scores(w)
     tau = entry["thresholds"]
     lev = o.assign_levels(C, tau, w.num_levels, 0, w.kv_block)
     fr = []
@@ -95,7 +113,7 @@ def match_ranked(w: W.Workload, entry: dict) -> dict:
         c = int(round(float(((lev >= 0) & (lev <= l)).sum(axis=-1).mean())))
         fr.append((c + 0.5) / w.nkb)
     lev_r = o.assign_levels_ranked(z, fr, w.num_levels, w.n_dense_prefix, w.kv_block)
-    r = o.effective_flops(lev_r, w.N, w.q_block, w.kv_block, w.d) / w.dense_flops()
+    r = rho_of(w, lev_r)
     print(f"{w.name}: ranked fractions {fr} rho={r:.5f} (thresholds: {entry['rho']:.5f}) "
           f"in {time.time()-t0:.1f}s", flush=True)
     out = dict(entry)
@@ -106,7 +124,7 @@ def match_ranked(w: W.Workload, entry: dict) -> dict:
 def main(argv):
     ranked = "--ranked" in argv
     argv = [a for a in argv if a != "--ranked"]
-    names = argv or [n for n, w in W.WORKLOADS.items() if w.target_rho is not None]
+    names = argv or [n for n, w in W.WORKLOADS.items() if w.target_rho is not None and not (ranked and w.causal)]
     table = {}
     if os.path.exists(W.THRESHOLDS_FILE):
         with open(W.THRESHOLDS_FILE) as f:

@@ -471,13 +471,16 @@ def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, 
             total += float(np.einsum("xij,i,j->", sel, m, rows_l))
             continue
         P = 1 << l
-        pairs = np.zeros((len(m), len(n)))                       # visible (row, pooled row) pairs
-        for i in range(len(m)):
-            rows = np.arange(i * q_block, i * q_block + int(m[i]))
-            for j in range(len(n)):
-                lo, hi = (j * kv_block) // P, -(-(j * kv_block + int(n[j])) // P)
-                last = np.minimum((np.arange(lo, hi) + 1) * P, N) - 1
-                pairs[i, j] = float((last[None, :] <= rows[:, None]).sum())
+        # last token of pooled row p of block j (p < kv_block / P); rows past the block: never seen
+        p = np.arange(kv_block // P)
+        last = (np.arange(len(n))[:, None] * kv_block + (p[None, :] + 1) * P).astype(np.int64)
+        last = np.minimum(last, N) - 1
+        last = np.where(p[None, :] * P < n[:, None], last, np.iinfo(np.int64).max // 2)
+        # query rows r0 .. r1-1 of block i see pooled row p when r >= last: r1 - max(r0, last) rows
+        r0 = (np.arange(len(m)) * q_block)[:, None, None]
+        r1 = r0 + m.astype(np.int64)[:, None, None]
+        seen = np.clip(r1 - np.maximum(r0, last[None, :, :]), 0, None)
+        pairs = seen.sum(axis=-1).astype(np.float64)             # [nqb, nkb]
         total += float(np.einsum("xij,ij->", sel, pairs))
     return 4.0 * d * total
 

@@ -46,6 +46,7 @@ class Workload:
     target_rho: Optional[float] = None   # FLOP fraction the thresholds are calibrated to
     n_dense_prefix: int = 0              # tokens whose KV blocks are always kept at level 0
     fixed_thresholds: Optional[Tuple[float, ...]] = None
+    causal: bool = False                 # query row r sees tokens 0..r only
     description: str = field(default="", compare=False)
 
     @property
@@ -86,8 +87,9 @@ class Workload:
         return tuple(float(x) for x in entry["ranked_fractions"][: self.num_levels])
 
     def dense_flops(self) -> float:
-        """4*B*H*N^2*d: QK^T plus PV of dense attention."""
-        return 4.0 * self.B * self.H * self.N * self.N * self.d
+        """4*B*H*N^2*d: QK^T plus PV of dense attention (causal: the N(N+1)/2 visible pairs)."""
+        pairs = self.N * (self.N + 1) / 2 if self.causal else float(self.N) * self.N
+        return 4.0 * self.B * self.H * pairs * self.d
 
 
 WORKLOADS = {
@@ -107,6 +109,10 @@ WORKLOADS = {
         name="qwen7b", index=3, B=1, H=28, H_kv=4, d=128, grid=(16, 32, 32), n_text=0,
         dtype="bf16", q_block=64, target_rho=0.35,
         description="Qwen2.5-VL-7B-style GQA bidirectional attention, 16384 tokens, ~35% of dense FLOPs"),
+    "wan13b_causal": Workload(
+        name="wan13b_causal", index=5, B=1, H=12, H_kv=12, d=128, grid=(21, 30, 52), n_text=0,
+        dtype="bf16", q_block=128, ft_max=0.5, target_rho=0.09, causal=True,
+        description="Wan2.1-1.3B-style layer in causal use, 32760 tokens, ~91% sparsity of causal attention"),
     "wan14b": Workload(
         name="wan14b", index=4, B=1, H=40, H_kv=40, d=128, grid=(21, 45, 80), n_text=0,
         dtype="bf16", q_block=128, target_rho=0.09,

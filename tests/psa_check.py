@@ -104,7 +104,7 @@ def check_mask(gpu_levels: np.ndarray, ora: dict, tau, L: int, n_dense_prefix: i
 
 
 def check_mask_ranked(gpu_levels: np.ndarray, ora: dict, counts, L: int, n_dense_prefix: int,
-                      kv_block: int = 64, label: str = ""):
+                      kv_block: int = 64, label: str = "", check_counts: bool = True):
     """Ranked rule. Every row must hold exactly K_l - K_{l-1} blocks at level l (checked
     on rows without forced blocks) -- unique whatever the order of near-ties. A block
     may differ from the oracle only when its level is the rule's level for some rank in
@@ -121,7 +121,7 @@ def check_mask_ranked(gpu_levels: np.ndarray, ora: dict, counts, L: int, n_dense
                 return l
         return L
 
-    if n_dense_prefix == 0:
+    if n_dense_prefix == 0 and check_counts:
         flat = gpu_levels.reshape(-1, gpu_levels.shape[-1])
         for l in range(L):
             want = K[l] - (K[l - 1] if l else 0)

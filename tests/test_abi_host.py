@@ -56,7 +56,7 @@ def test_sizes(psa):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 1), (dict(N=-5), 1), (dict(H=12, H_kv=5), 1), (dict(num_levels=0), 1),
-    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(causal=2), 1), (dict(causal=-1), 1),
     (dict(d=96), 2), (dict(q_block=32), 2), (dict(kv_block=128), 2), (dict(num_levels=5), 2),
     (dict(N=64 * 2048 + 1), 2), (dict(B=2, H=40000, H_kv=40000, N=64), 2),
 ])

@@ -420,6 +420,23 @@ def test_causal_mask_equals_mask_of_truncated_problem(rule):
         np.testing.assert_array_equal(m["levels"][:, :, i, :nv], expect)
 
 
+def test_causal_effective_flops_brute_force():
+    r = rng(67)
+    for N, bq in [(333, 128), (700, 64), (64, 128), (1, 64)]:
+        nqb, nkb = -(-N // bq), -(-N // 64)
+        lev = r.integers(-1, 4, size=(1, 2, nqb, nkb)).astype(np.int8)
+        pairs = 0
+        for h, i, j in np.ndindex(2, nqb, nkb):
+            l = int(lev[0, h, i, j])
+            if l < 0:
+                continue
+            P, nj = 1 << l, min(64, N - 64 * j)
+            for prow in range((64 * j) // P, -(-(64 * j + nj) // P)):
+                last = min((prow + 1) * P, N) - 1
+                pairs += sum(1 for row in range(i * bq, min((i + 1) * bq, N)) if row >= last)
+        assert o.effective_flops(lev, N, bq, 64, 8, causal=True) == 4 * 8 * pairs
+
+
 def test_causal_effective_flops_closed_form():
     N, d = 300, 8
     lev = np.zeros((1, 1, 3, 5), dtype=np.int8)
