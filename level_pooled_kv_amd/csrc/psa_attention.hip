@@ -13,7 +13,8 @@
 //  * One workgroup per (batch, head, query block); NW waves of 32 query rows each.
 //    Workgroup ids are remapped so that the eight XCDs each take a contiguous run
 //    of query blocks of the same heads (dispatch is round-robin over XCDs), which
-//    keeps the K/V rows those blocks share in one XCD's L2.
+//    keeps the K/V rows those blocks share in one XCD's L2. Under causal use the
+//    runs are made of (i, nqb-1-i) pairs of equal work, heavy halves first.
 //  * The level-map row is compacted in LDS into per-level lists of block indices.
 //    A hardware tile is always 64 key rows of ONE level: 1 block at level 0,
 //    2 at level 1, 4 at level 2, 8 at level 3. Within a tile every key carries the
@@ -64,9 +65,28 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bid = blockIdx.x;
-  const int item = (bid & 7) * per_xcd + (bid >> 3);
-  if (item >= total_items) return;
-  const int bh = item / nqb, qi = item - bh * nqb;
+  int bh, qi;
+  if (causal && (nqb & 1) == 0) {
+    // Causal: query block i sees about i + 1 blocks, so the pair (i, nqb-1-i) always
+    // carries the same work. Each XCD takes a contiguous run of pairs (balanced work, one
+    // head's K/V in one L2) and starts the heavy halves first, in decreasing order, so
+    // the light halves fill the tail.
+    const int ppx = per_xcd >> 1, k = bid >> 3;
+    const int u = k < ppx ? k : 2 * ppx - 1 - k;
+    const int pair = (bid & 7) * ppx + u;
+    if (pair >= (total_items >> 1)) return;
+    const int hq = nqb >> 1;
+    bh = pair / hq;
+    const int pi = pair - bh * hq;
+    qi = k < ppx ? nqb - 1 - pi : pi;
+  } else {
+    const int slot = (bid & 7) * per_xcd + (bid >> 3);
+    if (slot >= total_items) return;
+    bh = slot / nqb;
+    qi = slot - bh * nqb;
+    if (causal) qi = nqb - 1 - qi;   // heavier (later) query blocks first
+  }
+  const int item = bh * nqb + qi;
   const int b = bh / H, h = bh - b * H;
   const int bkv = b * H_kv + h / (H / H_kv);
 
@@ -371,7 +391,8 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 template <typename T, int D, int NW>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   const int total = a.B * a.H * a.nqb;
-  const int per = (total + 7) / 8;
+  // slots per XCD; causal with an even nqb hands out whole (i, nqb-1-i) pairs
+  const int per = a.causal && a.nqb % 2 == 0 ? 2 * ((total / 2 + 7) / 8) : (total + 7) / 8;
   const float cs = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((pyramid_attn_fwd_kernel<T, D, NW>), dim3(8 * per), dim3(NW * 64), 0, stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
