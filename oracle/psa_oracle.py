@@ -16,7 +16,8 @@ method as the pages describe it:
   KV-block importance, attention that keeps the probability distribution
   consistent); ablation paragraph (threshold-based assignment preferred to
   quantile-based; multi-level masks preferred to binary ones); paragraph on
-  causal use (generation) and bidirectional use (understanding).
+  causal use (generation) and bidirectional use (understanding); the ablation's
+  cosine-similarity constraint (no formula given: see key_similarity).
 * skillmd.com "Psa Pyramid Sparse Attention", sections "Pooled KV cache
   creation" (pool factor 2**level, average pooling over tokens), "Block
   importance scoring" (query against the block's mean key) and "Level
@@ -275,6 +276,70 @@ def apply_causal(C: np.ndarray, lev: np.ndarray, N: int, q_block: int, kv_block:
     lev[..., diag] = 0
     lev[..., ~vis] = -1
     return C, lev
+
+
+# ----------------------------------------------------------------------------
+# O4c: cosine-similarity constraint (top168.com, ablation paragraph)
+# ----------------------------------------------------------------------------
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    """cos(a, b); 0 when either vector is zero (a zero vector has no direction)."""
+    na, nb = float(np.linalg.norm(a)), float(np.linalg.norm(b))
+    if na == 0.0 or nb == 0.0:
+        return 0.0
+    return float(np.dot(a, b)) / (na * nb)
+
+
+def key_similarity(k: np.ndarray, kv_block: int, num_levels: int) -> np.ndarray:
+    """sim[b, g, j, l-1] for levels l = 1..L-1.
+
+    The article reports that a cosine-similarity constraint helps on some tasks but
+    gives no formula. Reading: a pooled key stands for its tokens well when it points
+    the way they do, so a level-l pool group scores the mean over its tokens of
+    cos(k_t, group mean); block j scores the smallest of its level-l groups (the
+    worst pooled key it would contribute)."""
+    k = np.asarray(k, dtype=np.float64)
+    B, H_kv, N, _ = k.shape
+    nkb = -(-N // kv_block)
+    sim = np.ones((B, H_kv, nkb, max(num_levels - 1, 0)))
+    for b in range(B):
+        for g in range(H_kv):
+            for j in range(nkb):
+                lo, hi = j * kv_block, min((j + 1) * kv_block, N)
+                for l in range(1, num_levels):
+                    P = 1 << l
+                    worst = np.inf
+                    for s0 in range(lo, hi, P):
+                        grp = k[b, g, s0:min(s0 + P, hi)]
+                        mean = grp.mean(axis=0)
+                        worst = min(worst, float(np.mean([cosine(t, mean) for t in grp])))
+                    sim[b, g, j, l - 1] = worst
+    return sim
+
+
+def similarity_cap(sim: np.ndarray, threshold: float) -> np.ndarray:
+    """cap[..., j] = the coarsest level l such that every level 1..l has sim >= threshold
+    (level 0 always qualifies). The threshold is compared as the float32 the library gets."""
+    thr = float(np.float32(threshold))
+    cap = np.zeros(sim.shape[:-1], dtype=np.int8)
+    ok = np.ones(sim.shape[:-1], dtype=bool)
+    for l in range(1, sim.shape[-1] + 1):
+        ok &= sim[..., l - 1] >= thr
+        cap[ok] = l
+    return cap
+
+
+def apply_similarity_cap(levels: np.ndarray, sim: np.ndarray, threshold: float) -> np.ndarray:
+    """A retained block takes min(level, cap of its KV block in the head's KV group);
+    pruned blocks stay pruned. levels [B,H,nqb,nkb], sim [B,H_kv,nkb,L-1]."""
+    B, H = levels.shape[:2]
+    H_kv = sim.shape[1]
+    cap = similarity_cap(sim, threshold)                        # [B, H_kv, nkb]
+    out = levels.copy()
+    for h in range(H):
+        c = cap[:, kv_head_of(h, H, H_kv)][:, None, :]          # [B, 1, nkb]
+        out[:, h] = np.where(levels[:, h] >= 0, np.minimum(levels[:, h], c), -1)
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -321,6 +321,84 @@ def test_ranked_dense_prefix_forced_after_ranking():
     np.testing.assert_array_equal(forced["rank"], plain["rank"])
 
 
+# ----------------------------------------------------------------------------- cosine-similarity constraint
+
+def brute_group_score(keys):
+    """mean over the group's tokens of cos(token, group mean), in plain float loops"""
+    d = len(keys[0])
+    mean = [math.fsum(k[c] for k in keys) / len(keys) for c in range(d)]
+    nm = math.sqrt(math.fsum(x * x for x in mean))
+    out = []
+    for k in keys:
+        nk = math.sqrt(math.fsum(x * x for x in k))
+        out.append(0.0 if nk == 0 or nm == 0 else math.fsum(a * b for a, b in zip(k, mean)) / (nk * nm))
+    return math.fsum(out) / len(out)
+
+
+def test_similarity_brute_force_with_ragged_block():
+    k = rng(70).standard_normal((1, 2, 150, 5))          # blocks of 64, 64, 22 tokens
+    sim = o.key_similarity(k, 64, 4)
+    assert sim.shape == (1, 2, 3, 3)
+    for g, j, l in np.ndindex(2, 3, 3):
+        lo, hi, P = 64 * j, min(64 * j + 64, 150), 2 ** (l + 1)
+        ref = min(brute_group_score(list(k[0, g, s0:min(s0 + P, hi)])) for s0 in range(lo, hi, P))
+        assert abs(sim[0, g, j, l] - ref) < 1e-12
+
+
+def test_similarity_closed_forms():
+    # level-1 pairs of unit keys at angle phi: the mean bisects them, each cosine is cos(phi/2)
+    d, phis = 2, np.linspace(0.1, 3.0, 32)
+    k = np.zeros((1, 1, 64, d))
+    for p, phi in enumerate(phis):
+        k[0, 0, 2 * p] = (1.0, 0.0)
+        k[0, 0, 2 * p + 1] = (math.cos(phi), math.sin(phi))
+    sim = o.key_similarity(k, 64, 2)
+    assert abs(sim[0, 0, 0, 0] - math.cos(phis.max() / 2)) < 1e-12
+    # identical keys: every level scores 1; opposite keys: the mean is zero, cosine 0
+    same = np.tile(rng(71).standard_normal((1, 1, 1, 6)), (1, 1, 64, 1))
+    np.testing.assert_allclose(o.key_similarity(same, 64, 4), 1.0, rtol=0, atol=1e-12)
+    opp = same.copy()
+    opp[0, 0, 1::2] *= -1
+    assert np.all(o.key_similarity(opp, 64, 4)[0, 0, 0] == 0.0)
+
+
+def test_similarity_invariances():
+    k = rng(72).standard_normal((1, 1, 128, 6))
+    base = o.key_similarity(k, 64, 4)
+    Q, _ = np.linalg.qr(rng(73).standard_normal((6, 6)))
+    np.testing.assert_allclose(o.key_similarity(k @ Q, 64, 4), base, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o.key_similarity(3.5 * k, 64, 4), base, rtol=0, atol=1e-12)
+
+
+def test_similarity_cap_rules():
+    sim = np.array([[[[0.9, 0.8, 0.7], [0.5, 0.95, 0.95], [0.99, 0.99, 0.2], [1.0, 1.0, 1.0]]]])
+    np.testing.assert_array_equal(o.similarity_cap(sim, 0.75), [[[2, 0, 2, 3]]])
+    np.testing.assert_array_equal(o.similarity_cap(sim, -1.0), [[[3, 3, 3, 3]]])
+    np.testing.assert_array_equal(o.similarity_cap(sim, 1.5), [[[0, 0, 0, 0]]])
+    lev = np.array([[[[3, 3, 3, 3], [-1, 1, 0, 2]]]], dtype=np.int8)          # B1 H1 nqb2 nkb4
+    np.testing.assert_array_equal(o.apply_similarity_cap(lev, sim, 0.75), [[[[2, 0, 2, 3], [-1, 0, 0, 2]]]])
+
+
+def test_similarity_cap_monotone_and_gqa():
+    k = rng(74).standard_normal((1, 2, 512, 8))
+    q = rng(75).standard_normal((1, 4, 512, 8))
+    lev = o.estimate_mask(q, k, 64, 64, (0.2, 0.4, 0.6, 0.8), 4, 0.4)["levels"]
+    sim = o.key_similarity(k, 64, 4)
+    prev = lev.astype(int)
+    for thr in (-1.0, 0.3, 0.5, 0.6, 0.7, 1.01):
+        cur = o.apply_similarity_cap(lev, sim, thr).astype(int)
+        assert np.all((cur >= 0) == (lev >= 0))                                 # pruning unchanged
+        assert np.all(cur[lev >= 0] <= prev[lev >= 0])                          # never coarser
+        prev = cur
+    assert np.all(prev[lev >= 0] == 0)
+    cap = o.similarity_cap(sim, 0.5)
+    out = o.apply_similarity_cap(lev, sim, 0.5)
+    for h in range(4):                                                          # heads 0,1 -> KV 0
+        g = h // 2
+        exp = np.where(lev[0, h] >= 0, np.minimum(lev[0, h], cap[0, g][None, :]), -1)
+        np.testing.assert_array_equal(out[0, h], exp)
+
+
 # ----------------------------------------------------------------------------- causal use
 
 def test_causal_blocks_closed_form():
