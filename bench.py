@@ -196,6 +196,9 @@ def main():
     ap.add_argument("--fractions", default=None,
                     help="ranked rule: comma-separated cumulative block fractions per level "
                          "(default: the workload's, matched to its threshold mask's mean level counts)")
+    ap.add_argument("--similarity", type=float, default=None, metavar="THRESHOLD",
+                    help="add the cosine-similarity constraint: the pyramid step also computes the key "
+                         "similarity and the level map is capped at THRESHOLD before attention")
     ap.add_argument("--compare-rules", action="store_true",
                     help="only compare the output error of threshold / ranked / binary masks at equal "
                          "FLOP fraction against dense attention, print that JSON line and exit")
@@ -243,19 +246,25 @@ def main():
     k_pyr = torch.empty((w.B, w.H_kv, R, w.d), dtype=dt, device=dev)
     v_pyr = torch.empty_like(k_pyr)
     k_bar = torch.empty((w.B, w.H_kv, prob.nkb, w.d), dtype=torch.float32, device=dev)
+    k_sim = torch.empty((w.B, w.H_kv, prob.nkb, max(w.num_levels - 1, 1)), dtype=torch.float32, device=dev)
     level_map = torch.empty((w.B, w.H, prob.nqb, prob.nkb), dtype=torch.int8, device=dev)
     ws = torch.empty(prob.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK), dtype=torch.uint8, device=dev)
     o = torch.empty_like(qd)
 
     def step(ev=None):
         if ev: ev[0].record()
-        psa.psa_build_pyramid(prob, kd, vd, k_pyr, v_pyr, k_bar)
+        if args.similarity is None:
+            psa.psa_build_pyramid(prob, kd, vd, k_pyr, v_pyr, k_bar)
+        else:
+            psa.psa_build_pyramid_sim(prob, kd, vd, k_pyr, v_pyr, k_bar, k_sim)
         if ev: ev[1].record()
         if fractions is None:
             psa.psa_estimate_mask(prob, qd, k_bar, tau, w.n_dense_prefix, level_map=level_map, workspace=ws)
         else:
             psa.psa_estimate_mask_ranked(prob, qd, k_bar, fractions, w.n_dense_prefix, level_map=level_map,
                                          workspace=ws)
+        if args.similarity is not None:
+            psa.psa_apply_similarity_cap(prob, k_sim, args.similarity, level_map)
         if ev: ev[2].record()
         psa.psa_attention_fwd(prob, qd, kd, vd, k_pyr, v_pyr, level_map, o=o)
         if ev: ev[3].record()
@@ -297,7 +306,8 @@ def main():
                    "N": w.N, "d": w.d, "q_block": w.q_block, "kv_block": w.kv_block,
                    "num_levels": w.num_levels, "causal": w.causal, "parallelism": "single GPU",
                    **({"rule": "threshold", "thresholds": list(tau)} if fractions is None
-                      else {"rule": "ranked", "fractions": fractions})},
+                      else {"rule": "ranked", "fractions": fractions}),
+                   **({} if args.similarity is None else {"similarity_threshold": args.similarity})},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": attention_kernel_name(w.d, w.q_block, w.dtype)},

@@ -10,6 +10,7 @@
  *   psa_build_pyramid  — average-pooled K/V levels 1..L-1 and per-block mean keys
  *   psa_estimate_mask  — block importance and the threshold-based level map
  *   psa_estimate_mask_ranked — the same with a fixed share of ranked blocks per level
+ *   psa_build_pyramid_sim, psa_apply_similarity_cap — the cosine-similarity constraint
  *   psa_attention_fwd  — attention over mixed-resolution keys, one softmax
  *
  * Tensors (all row-major, contiguous, head_dim innermost):
@@ -109,6 +110,33 @@ psa_status_t psa_check_problem(const psa_problem_t* prob);
  */
 psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const void* v,
                                void* k_pyr, void* v_pyr, float* k_bar, hipStream_t stream);
+
+/*
+ * Step 1 plus the key similarity of the cosine-similarity constraint (the
+ * top168.com ablation paragraph reports that such a constraint helps on some tasks
+ * and gives no formula; this is the library's reading). Same outputs as
+ * psa_build_pyramid, and for KV block j and level l = 1..L-1
+ *   k_sim[b, g, j, l-1] = min over the level-l pool groups G of block j of
+ *                         (1/|G|) sum_{t in G} cos(k_t, mean of G),
+ * with cos = 0 when either vector is zero: 1 when every group's keys point the
+ * same way, lower as they spread. Float32, computed from the same registers as
+ * the pyramid (K is read once). k_sim [B, H_kv, nkb, L-1] float32; may be NULL
+ * when num_levels == 1 (then nothing is written).
+ */
+psa_status_t psa_build_pyramid_sim(const psa_problem_t* prob, const void* k, const void* v,
+                                   void* k_pyr, void* v_pyr, float* k_bar, float* k_sim,
+                                   hipStream_t stream);
+
+/*
+ * The cosine-similarity constraint applied to a level map in place: a retained
+ * block at level l > 0 of query head h takes the coarsest level l' <= l such that
+ * k_sim[b, g(h), j, m-1] >= threshold for every m = 1..l' (level 0 if level 1
+ * already fails). Pruned blocks, level-0 blocks and values outside [-1, L-1] are
+ * left as they are; the map is then ready for psa_attention_fwd. Nothing to do when
+ * num_levels == 1 (k_sim may then be NULL). threshold: any non-NaN float.
+ */
+psa_status_t psa_apply_similarity_cap(const psa_problem_t* prob, const float* k_sim, float threshold,
+                                      int8_t* level_map, hipStream_t stream);
 
 /*
  * Step 2, the multi-level mask ("a multi-level mask generator that assigns a

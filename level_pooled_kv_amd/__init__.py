@@ -31,7 +31,8 @@ PSA_F32, PSA_BF16 = 0, 1
 PSA_WS_ESTIMATE_MASK, PSA_WS_ATTENTION_FWD = 0, 1
 
 EXPORTED = (
-    "psa_pyramid_rows", "psa_workspace_bytes", "psa_check_problem", "psa_build_pyramid",
+    "psa_pyramid_rows", "psa_workspace_bytes", "psa_check_problem", "psa_build_pyramid", "psa_build_pyramid_sim",
+    "psa_apply_similarity_cap",
     "psa_estimate_mask", "psa_estimate_mask_ranked", "psa_attention_fwd", "psa_status_string", "psa_last_error",
 )
 
@@ -52,6 +53,10 @@ _lib.psa_workspace_bytes.argtypes, _lib.psa_workspace_bytes.restype = [_P, ctype
 _lib.psa_check_problem.argtypes, _lib.psa_check_problem.restype = [_P], _st
 _lib.psa_build_pyramid.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.psa_build_pyramid.restype = _st
+_lib.psa_build_pyramid_sim.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.psa_build_pyramid_sim.restype = _st
+_lib.psa_apply_similarity_cap.argtypes = [_P, _vp, ctypes.c_float, _vp, _vp]
+_lib.psa_apply_similarity_cap.restype = _st
 _lib.psa_estimate_mask.argtypes = [_P, _vp, _vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int32, _vp, _vp,
                                    _vp, _sz, _vp]
 _lib.psa_estimate_mask.restype = _st
@@ -134,10 +139,7 @@ def _need(t: torch.Tensor, name: str, shape, dtype):
                          f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
 
 
-def psa_build_pyramid(prob: Problem, k: torch.Tensor, v: torch.Tensor, k_pyr: Optional[torch.Tensor] = None,
-                      v_pyr: Optional[torch.Tensor] = None, k_bar: Optional[torch.Tensor] = None, stream=None):
-    """Step 1: pooled K/V levels 1..L-1 ([B,H_kv,R,d]) and block mean keys ([B,H_kv,nkb,d] float32).
-    Missing outputs are allocated. Returns (k_pyr, v_pyr, k_bar)."""
+def _pyramid_buffers(prob: Problem, k, v, k_pyr, v_pyr, k_bar):
     dt = prob.torch_dtype
     kv_shape = (prob.B, prob.H_kv, prob.N, prob.d)
     _need(k, "k", kv_shape, dt)
@@ -147,12 +149,48 @@ def psa_build_pyramid(prob: Problem, k: torch.Tensor, v: torch.Tensor, k_pyr: Op
         k_pyr = torch.empty((prob.B, prob.H_kv, max(R, 1), prob.d), dtype=dt, device=k.device)
     if v_pyr is None:
         v_pyr = torch.empty((prob.B, prob.H_kv, max(R, 1), prob.d), dtype=dt, device=k.device)
+    if R > 0:
+        _need(k_pyr, "k_pyr", (prob.B, prob.H_kv, R, prob.d), dt)
+        _need(v_pyr, "v_pyr", (prob.B, prob.H_kv, R, prob.d), dt)
     if k_bar is None:
         k_bar = torch.empty((prob.B, prob.H_kv, prob.nkb, prob.d), dtype=torch.float32, device=k.device)
     _need(k_bar, "k_bar", (prob.B, prob.H_kv, prob.nkb, prob.d), torch.float32)
+    return k_pyr, v_pyr, k_bar
+
+
+def psa_build_pyramid(prob: Problem, k: torch.Tensor, v: torch.Tensor, k_pyr: Optional[torch.Tensor] = None,
+                      v_pyr: Optional[torch.Tensor] = None, k_bar: Optional[torch.Tensor] = None, stream=None):
+    """Step 1: pooled K/V levels 1..L-1 ([B,H_kv,R,d]) and block mean keys ([B,H_kv,nkb,d] float32).
+    Missing outputs are allocated. Returns (k_pyr, v_pyr, k_bar)."""
+    k_pyr, v_pyr, k_bar = _pyramid_buffers(prob, k, v, k_pyr, v_pyr, k_bar)
     _check(_lib.psa_build_pyramid(ctypes.byref(prob.c()), _ptr(k), _ptr(v), _ptr(k_pyr), _ptr(v_pyr),
                                   _ptr(k_bar), _stream(stream)))
     return k_pyr, v_pyr, k_bar
+
+
+def psa_build_pyramid_sim(prob: Problem, k: torch.Tensor, v: torch.Tensor, k_pyr: Optional[torch.Tensor] = None,
+                          v_pyr: Optional[torch.Tensor] = None, k_bar: Optional[torch.Tensor] = None,
+                          k_sim: Optional[torch.Tensor] = None, stream=None):
+    """Step 1 plus the key similarity per pooled level ([B,H_kv,nkb,L-1] float32).
+    Returns (k_pyr, v_pyr, k_bar, k_sim)."""
+    k_pyr, v_pyr, k_bar = _pyramid_buffers(prob, k, v, k_pyr, v_pyr, k_bar)
+    shape = (prob.B, prob.H_kv, prob.nkb, max(prob.num_levels - 1, 0))
+    if k_sim is None:
+        k_sim = torch.empty(shape, dtype=torch.float32, device=k.device)
+    _need(k_sim, "k_sim", shape, torch.float32)
+    _check(_lib.psa_build_pyramid_sim(ctypes.byref(prob.c()), _ptr(k), _ptr(v), _ptr(k_pyr), _ptr(v_pyr),
+                                      _ptr(k_bar), _ptr(k_sim) if k_sim.numel() else None, _stream(stream)))
+    return k_pyr, v_pyr, k_bar, k_sim
+
+
+def psa_apply_similarity_cap(prob: Problem, k_sim: torch.Tensor, threshold: float, level_map: torch.Tensor,
+                             stream=None):
+    """Caps the levels of level_map in place by the key similarity; returns level_map."""
+    _need(k_sim, "k_sim", (prob.B, prob.H_kv, prob.nkb, max(prob.num_levels - 1, 0)), torch.float32)
+    _need(level_map, "level_map", (prob.B, prob.H, prob.nqb, prob.nkb), torch.int8)
+    _check(_lib.psa_apply_similarity_cap(ctypes.byref(prob.c()), _ptr(k_sim) if k_sim.numel() else None,
+                                         ctypes.c_float(float(threshold)), _ptr(level_map), _stream(stream)))
+    return level_map
 
 
 def _mask_buffers(prob: Problem, q, k_bar, level_map, cmass, want_cmass, workspace):

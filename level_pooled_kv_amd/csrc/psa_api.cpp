@@ -129,11 +129,9 @@ psa_status_t psa_check_problem(const psa_problem_t* prob) {
   return check_problem(prob);
 }
 
-psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const void* v, void* k_pyr,
-                               void* v_pyr, float* k_bar, hipStream_t stream) {
-  clear_error();
-  psa_status_t s = check_problem(prob);
-  if (s != PSA_OK) return s;
+static psa_status_t build_pyramid_common(const psa_problem_t* prob, const void* k, const void* v, void* k_pyr,
+                                         void* v_pyr, float* k_bar, float* k_sim, hipStream_t stream,
+                                         const char* what) {
   REQUIRE_PTR(k, "k");
   REQUIRE_PTR(v, "v");
   REQUIRE_PTR(k_bar, "k_bar");
@@ -143,6 +141,7 @@ psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const v
   }
   psa::PyramidArgs a{};
   a.k = k; a.v = v; a.k_pyr = k_pyr; a.v_pyr = v_pyr; a.k_bar = k_bar;
+  a.k_sim = prob->num_levels > 1 ? k_sim : nullptr;
   a.B = prob->B; a.H_kv = prob->H_kv; a.N = prob->N; a.d = prob->d;
   a.nkb = (int)ceil_div(prob->N, psa::kKvBlock);
   a.L = prob->num_levels;
@@ -150,7 +149,42 @@ psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const v
   a.pyr_rows = pyramid_rows(prob);
   int rows[psa::kMaxLevels];
   level_offsets(prob, a.off, rows);
-  return hip_status(psa::launch_pyramid(a, stream), "psa_build_pyramid launch");
+  return hip_status(psa::launch_pyramid(a, stream), what);
+}
+
+psa_status_t psa_build_pyramid(const psa_problem_t* prob, const void* k, const void* v, void* k_pyr,
+                               void* v_pyr, float* k_bar, hipStream_t stream) {
+  clear_error();
+  psa_status_t s = check_problem(prob);
+  if (s != PSA_OK) return s;
+  return build_pyramid_common(prob, k, v, k_pyr, v_pyr, k_bar, nullptr, stream, "psa_build_pyramid launch");
+}
+
+psa_status_t psa_build_pyramid_sim(const psa_problem_t* prob, const void* k, const void* v, void* k_pyr,
+                                   void* v_pyr, float* k_bar, float* k_sim, hipStream_t stream) {
+  clear_error();
+  psa_status_t s = check_problem(prob);
+  if (s != PSA_OK) return s;
+  if (prob->num_levels > 1) REQUIRE_PTR(k_sim, "k_sim");
+  return build_pyramid_common(prob, k, v, k_pyr, v_pyr, k_bar, k_sim, stream, "psa_build_pyramid_sim launch");
+}
+
+psa_status_t psa_apply_similarity_cap(const psa_problem_t* prob, const float* k_sim, float threshold,
+                                      int8_t* level_map, hipStream_t stream) {
+  clear_error();
+  psa_status_t s = check_problem(prob);
+  if (s != PSA_OK) return s;
+  if (isnan(threshold)) return fail(PSA_ERR_INVALID_ARGUMENT, "threshold is NaN");
+  REQUIRE_PTR(level_map, "level_map");
+  if (prob->num_levels < 2) return PSA_OK;   // nothing is pooled: nothing to cap
+  REQUIRE_PTR(k_sim, "k_sim");
+  psa::CapArgs a{};
+  a.level_map = level_map; a.k_sim = k_sim; a.threshold = threshold;
+  a.B = prob->B; a.H = prob->H; a.H_kv = prob->H_kv;
+  a.nqb = (int)ceil_div(prob->N, prob->q_block);
+  a.nkb = (int)ceil_div(prob->N, psa::kKvBlock);
+  a.L = prob->num_levels;
+  return hip_status(psa::launch_similarity_cap(a, stream), "psa_apply_similarity_cap launch");
 }
 
 // Checks shared by both mask entry points, then the launch. Exactly one of tau and

@@ -66,4 +66,40 @@ template <> __device__ __forceinline__ U128 pack16<float>(const float* in) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Value of lane (lane ^ M), from VALU cross-lane ops only (no LDS round trip): DPP
+// quad permutes for 1 and 2, a half-row mirror (lane ^ 7) then a quad reverse (^ 3)
+// for 4, a row rotate by 8 for 8, and the gfx950 row swaps for 16 and 32 (with
+// a = b = x, permlane16_swap returns {x[l & ~16], x[l | 16]} per lane and
+// permlane32_swap {x[l & ~32], x[l | 32]}).
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
+  else if constexpr (M == 4) {
+    const int m7 = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(m7, 0x1B, 0xF, 0xF, true);
+  } else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, true);
+  else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    static_assert(M == 32, "lane distance");
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? p[0] : p[1];
+  }
+}
+
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64); every lane
+// of a group receives its group's total.
+template <int G>
+__device__ __forceinline__ float group_sum(float x, int lane) {
+  if constexpr (G >= 2) x += __uint_as_float(xor_lane<1>(__float_as_uint(x), lane));
+  if constexpr (G >= 4) x += __uint_as_float(xor_lane<2>(__float_as_uint(x), lane));
+  if constexpr (G >= 8) x += __uint_as_float(xor_lane<4>(__float_as_uint(x), lane));
+  if constexpr (G >= 16) x += __uint_as_float(xor_lane<8>(__float_as_uint(x), lane));
+  if constexpr (G >= 32) x += __uint_as_float(xor_lane<16>(__float_as_uint(x), lane));
+  if constexpr (G >= 64) x += __uint_as_float(xor_lane<32>(__float_as_uint(x), lane));
+  return x;
+}
+
 }  // namespace psa

@@ -13,6 +13,7 @@ constexpr int kMaxKvBlocks = 2048; // per sequence (LDS capacity of the mask sor
 
 struct PyramidArgs {
   const void* k; const void* v; void* k_pyr; void* v_pyr; float* k_bar;
+  float* k_sim;                  // nullable: [B, H_kv, nkb, L-1] key similarity per pooled level
   int B, H_kv, N, d, nkb, L;
   bool bf16;
   int64_t pyr_rows;              // rows of the concatenated pyramid
@@ -47,7 +48,13 @@ struct AttnArgs {
   int rows[kMaxLevels];          // ceil(N / 2^l)
 };
 
+struct CapArgs {
+  int8_t* level_map; const float* k_sim; float threshold;
+  int B, H, H_kv, nqb, nkb, L;
+};
+
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t stream);
+hipError_t launch_similarity_cap(const CapArgs& a, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
 int mask_score_stride(int nkb);  // padded row length of the score workspace
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);

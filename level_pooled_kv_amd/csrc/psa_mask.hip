@@ -186,28 +186,6 @@ __device__ __forceinline__ float key_score(uint64_t k) {
   return __uint_as_float((key & 0x80000000u) ? key : (~key & 0x7fffffffu));
 }
 
-// Value of lane (lane ^ M), from VALU cross-lane ops only (no LDS round trip): DPP
-// quad permutes for 1 and 2, a half-row mirror (lane ^ 7) then a quad reverse (^ 3)
-// for 4, a row rotate by 8 for 8, and the gfx950 row swaps for 16 and 32 (with
-// a = b = x, permlane16_swap returns {x[l & ~16], x[l | 16]} per lane and
-// permlane32_swap {x[l & ~32], x[l | 32]}).
-template <int M>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
-  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
-  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
-  else if constexpr (M == 4) {
-    const int m7 = __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true);
-    return (uint32_t)__builtin_amdgcn_mov_dpp(m7, 0x1B, 0xF, 0xF, true);
-  } else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, true);
-  else if constexpr (M == 16) {
-    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? p[0] : p[1];
-  } else {
-    static_assert(M == 32, "lane distance");
-    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? p[0] : p[1];
-  }
-}
 template <int M>
 __device__ __forceinline__ uint64_t xor_lane64(uint64_t x, int lane) {
   const uint32_t lo = xor_lane<M>((uint32_t)x, lane);

@@ -145,6 +145,23 @@ def test_estimate_mask_ranked_rejects(psa):
     assert "cmass_out" in psa.last_error()
 
 
+def test_similarity_entry_points_reject(psa):
+    c = prob(psa).c()
+    f = psa.lib.psa_build_pyramid_sim
+    assert f(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1          # k_sim NULL with L = 4
+    assert "k_sim" in psa.last_error()
+    assert f(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, None) == 1
+    assert f(ctypes.byref(c), None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    g = psa.lib.psa_apply_similarity_cap
+    assert g(ctypes.byref(c), FAKE, ctypes.c_float(float("nan")), FAKE, None) == 1
+    assert g(ctypes.byref(c), None, ctypes.c_float(0.5), FAKE, None) == 1
+    assert g(ctypes.byref(c), FAKE, ctypes.c_float(0.5), None, None) == 1
+    c1 = prob(psa, num_levels=1).c()                # nothing pooled: a no-op that launches nothing
+    assert g(ctypes.byref(c1), None, ctypes.c_float(0.5), FAKE, None) == 0
+    bad = prob(psa, d=96).c()
+    assert g(ctypes.byref(bad), FAKE, ctypes.c_float(0.5), FAKE, None) == 2
+
+
 def test_attention_rejects(psa):
     c = prob(psa).c()
     f = psa.lib.psa_attention_fwd
