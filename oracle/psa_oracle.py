@@ -70,6 +70,8 @@ def round_to_io(x: np.ndarray, dtype: str) -> np.ndarray:
         return round_to_bf16(x)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "f64":          # no rounding (exact-arithmetic checks of the oracle itself)
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(dtype)
 
 
@@ -417,14 +419,16 @@ def estimate_mask_ranked(q: np.ndarray, k: np.ndarray, q_block: int, kv_block: i
 # ----------------------------------------------------------------------------
 
 def gather_keys(levels_row: np.ndarray, N: int, kv_block: int,
-                kpyr: Sequence[np.ndarray], vpyr: Sequence[np.ndarray], with_last: bool = False):
+                kpyr: Sequence[np.ndarray], vpyr: Sequence[np.ndarray], with_last: bool = False,
+                with_index: bool = False):
     """Keys, values and log pool sizes that one query block attends to.
 
     KV block j at level l contributes its pooled rows [j*b/2**l, ceil((j*b + n_j)/2**l))
     of level l (level 0: its tokens). kpyr/vpyr: per-level [N_l, d] arrays.
-    with_last: also return the last token each key averages (for causal masking)."""
+    with_last: also return the last token each key averages (for causal masking).
+    with_index: also return each key's (level, pooled row) (for scattering gradients)."""
     n_kv = block_sizes(N, kv_block)
-    ks, vs, lc, last = [], [], [], []
+    ks, vs, lc, last, idx = [], [], [], [], []
     for j, l in enumerate(levels_row):
         l = int(l)
         if l < 0:
@@ -436,12 +440,16 @@ def gather_keys(levels_row: np.ndarray, N: int, kv_block: int,
         vs.append(vpyr[l][lo:hi])
         lc.append(np.log(pool_counts(N, l)[lo:hi].astype(np.float64)))
         last.append(np.minimum((np.arange(lo, hi) + 1) * P, N) - 1)
+        idx.append(np.stack([np.full(hi - lo, l), np.arange(lo, hi)], axis=1))
     d = kpyr[0].shape[-1]
     if not ks:
         out = (np.zeros((0, d)), np.zeros((0, d)), np.zeros(0))
-        return out + (np.zeros(0, dtype=np.int64),) if with_last else out
+        extra = ((np.zeros(0, dtype=np.int64),) if with_last else ()) + \
+                ((np.zeros((0, 2), dtype=np.int64),) if with_index else ())
+        return out + extra
     out = (np.concatenate(ks), np.concatenate(vs), np.concatenate(lc))
-    return out + (np.concatenate(last),) if with_last else out
+    extra = ((np.concatenate(last),) if with_last else ()) + ((np.concatenate(idx),) if with_index else ())
+    return out + extra
 
 
 def attention_rows(qrows: np.ndarray, keys: np.ndarray, vals: np.ndarray, logc: np.ndarray,
@@ -495,6 +503,66 @@ def pyramid_attention(q: np.ndarray, kpyr_levels: Sequence[np.ndarray], vpyr_lev
         allowed = last[None, :] <= np.arange(r0, r1)[:, None] if causal else None
         O[b, h, r0:r1], LSE[b, h, r0:r1] = attention_rows(q[b, h, r0:r1], keys, vals, logc, scale, allowed)
     return O, LSE
+
+
+def pyramid_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, num_levels: int, level_map: np.ndarray,
+                          q_block: int, kv_block: int, scale: float, dO: np.ndarray, io_dtype: str = "f32",
+                          causal: bool = False) -> Dict[str, np.ndarray]:
+    """Gradients of sum(O * dO) with respect to q, k and v, the level map held fixed
+    (it is a discrete choice). The pages describe no backward pass; this is the
+    gradient of the forward as defined here.
+
+    Per query row r with weights P_rp = exp(a_rp - LSE_r) over its keys p:
+      dV_p += P_rp dO_r;  dP_rp = <dO_r, V_p>;  D_r = <dO_r, O_r>;
+      dA_rp = P_rp (dP_rp - D_r);  dq_r = scale sum_p dA_rp K_p;  dK_p += scale dA_rp q_r.
+    A pooled row is the mean of its c tokens, so its gradient reaches each of them
+    divided by c. The pooled keys and values are those the forward used (rounded to
+    the I/O dtype). Returns dq [B,H,N,d], dk, dv [B,H_kv,N,d] and the per-level
+    pooled gradients dk_levels / dv_levels (level 0 = the tokens' own share)."""
+    q = np.asarray(q, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    kp = [np.asarray(k, np.float64)] + [round_to_io(x, io_dtype) for x in build_pyramid(k, num_levels)[1:]]
+    vp = [np.asarray(v, np.float64)] + [round_to_io(x, io_dtype) for x in build_pyramid(v, num_levels)[1:]]
+    O, LSE = pyramid_attention(q, kp, vp, level_map, q_block, kv_block, scale, causal=causal)
+    dq = np.zeros_like(q)
+    dkl = [np.zeros_like(x) for x in kp]
+    dvl = [np.zeros_like(x) for x in vp]
+    nqb = -(-N // q_block)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, H_kv)
+            for i in range(nqb):
+                keys, vals, logc, last, idx = gather_keys(level_map[b, h, i], N, kv_block, [x[b, g] for x in kp],
+                                                          [x[b, g] for x in vp], with_last=True, with_index=True)
+                if keys.shape[0] == 0:
+                    continue
+                r0, r1 = i * q_block, min((i + 1) * q_block, N)
+                qr, dOr, Or = q[b, h, r0:r1], dO[b, h, r0:r1], O[b, h, r0:r1]
+                a = scale * (qr @ keys.T) + logc[None, :]
+                if causal:
+                    a = np.where(last[None, :] <= np.arange(r0, r1)[:, None], a, -np.inf)
+                fin = np.isfinite(LSE[b, h, r0:r1])[:, None]
+                P = np.where(fin, np.exp(a - np.where(fin, LSE[b, h, r0:r1][:, None], 0.0)), 0.0)
+                dP = dOr @ vals.T
+                Dr = np.sum(dOr * Or, axis=1, keepdims=True)
+                dA = P * (dP - Dr)
+                dq[b, h, r0:r1] = scale * (dA @ keys)
+                dK = scale * (dA.T @ qr)
+                dV = P.T @ dOr
+                for l in range(num_levels):
+                    sel = idx[:, 0] == l
+                    np.add.at(dkl[l][b, g], idx[sel, 1], dK[sel])
+                    np.add.at(dvl[l][b, g], idx[sel, 1], dV[sel])
+    dk = dkl[0].copy()
+    dv = dvl[0].copy()
+    for l in range(1, num_levels):
+        c = pool_counts(N, l).astype(np.float64)[:, None]
+        up = np.arange(N) >> l
+        dk += (dkl[l] / c)[:, :, up]
+        dv += (dvl[l] / c)[:, :, up]
+    return {"dq": dq, "dk": dk, "dv": dv, "dk_levels": dkl, "dv_levels": dvl, "O": O, "LSE": LSE}
 
 
 def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,

@@ -666,6 +666,80 @@ def test_effective_flops_closed_forms():
     assert o.effective_flops(lev, N, 64, 64, d) == 0.0
 
 
+# ----------------------------------------------------------------------------- backward
+
+def loss_and_grads(q, k, v, L, lev, bq, s, dO, causal=False):
+    g = o.pyramid_attention_bwd(q, k, v, L, lev, bq, 64, s, dO, io_dtype="f64", causal=causal)
+    return float(np.sum(g["O"] * dO)), g
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    # central differences of sum(O * dO) in float64 at a handful of coordinates per tensor
+    r = rng(80)
+    N, d, L, bq, s = 150, 3, 3, 64, 0.7
+    q, k, v = r.standard_normal((1, 2, N, d)), r.standard_normal((1, 1, N, d)), r.standard_normal((1, 1, N, d))
+    dO = r.standard_normal((1, 2, N, d))
+    lev = r.integers(-1, L, size=(1, 2, 3, 3)).astype(np.int8)
+    lev[..., 0] = np.maximum(lev[..., 0], 0)
+    _, g = loss_and_grads(q, k, v, L, lev, bq, s, dO, causal)
+    eps = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        for idx in [tuple(r.integers(0, n) for n in x.shape) for _ in range(12)] + [(0, 0, N - 1, 2)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            key = name[1:]
+            fp = loss_and_grads(**{**args, key: xp}, L=L, lev=lev, bq=bq, s=s, dO=dO, causal=causal)[0]
+            fm = loss_and_grads(**{**args, key: xm}, L=L, lev=lev, bq=bq, s=s, dO=dO, causal=causal)[0]
+            assert abs((fp - fm) / (2 * eps) - g[name][idx]) < 1e-6, (name, idx, (fp - fm) / (2 * eps), g[name][idx])
+
+
+def test_backward_dense_map_equals_torch_autograd():
+    r = rng(81)
+    N, d, s = 200, 8, 0.3
+    q, k, v = r.standard_normal((1, 2, N, d)), r.standard_normal((1, 2, N, d)), r.standard_normal((1, 2, N, d))
+    dO = r.standard_normal((1, 2, N, d))
+    for causal in (False, True):
+        lev = np.zeros((1, 2, 4, 4), dtype=np.int8)
+        g = o.pyramid_attention_bwd(q, k, v, 4, lev, 64, 64, s, dO, io_dtype="f64", causal=causal)
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=s)
+        out.backward(torch.from_numpy(dO))
+        for name, t in (("dq", qt), ("dk", kt), ("dv", vt)):
+            np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_pooled_gradient_spreads_evenly():
+    # With every block at level 3, a token's key gradient is its group's pooled gradient / 8
+    r = rng(82)
+    N, d = 128, 4
+    q, k, v = r.standard_normal((1, 1, N, d)), r.standard_normal((1, 1, N, d)), r.standard_normal((1, 1, N, d))
+    dO = r.standard_normal((1, 1, N, d))
+    lev = np.full((1, 1, 2, 2), 3, dtype=np.int8)
+    g = o.pyramid_attention_bwd(q, k, v, 4, lev, 64, 64, 0.5, dO, io_dtype="f64")
+    for t in (0, 7, 8, 77, 127):
+        np.testing.assert_allclose(g["dk"][0, 0, t], g["dk_levels"][3][0, 0, t // 8] / 8, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(g["dv"][0, 0, t], g["dv_levels"][3][0, 0, t // 8] / 8, rtol=0, atol=1e-14)
+    # dV of a pooled row is the sum of its attention weights times dO: columns of P sum over rows
+    np.testing.assert_allclose(g["dv_levels"][3].sum(axis=2), dO.sum(axis=2), rtol=0, atol=1e-10)
+
+
+def test_backward_gqa_sums_heads():
+    r = rng(83)
+    N, d = 256, 4
+    q, k, v = r.standard_normal((1, 4, N, d)), r.standard_normal((1, 2, N, d)), r.standard_normal((1, 2, N, d))
+    dO = r.standard_normal((1, 4, N, d))
+    lev = r.integers(-1, 4, size=(1, 4, 2, 4)).astype(np.int8)
+    g = o.pyramid_attention_bwd(q, k, v, 4, lev, 128, 64, 0.5, dO, io_dtype="f64")
+    rep = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    gm = o.pyramid_attention_bwd(q, rep[0], rep[1], 4, lev, 128, 64, 0.5, dO, io_dtype="f64")
+    np.testing.assert_allclose(g["dq"], gm["dq"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dk"], gm["dk"].reshape(1, 2, 2, N, d).sum(axis=2), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dv"], gm["dv"].reshape(1, 2, 2, N, d).sum(axis=2), rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- hand-worked example
 
 def test_worked_example():
