@@ -12,6 +12,7 @@
  *   psa_estimate_mask_ranked — the same with a fixed share of ranked blocks per level
  *   psa_build_pyramid_sim, psa_apply_similarity_cap — the cosine-similarity constraint
  *   psa_attention_fwd  — attention over mixed-resolution keys, one softmax
+ *   psa_attention_bwd  — its gradients with respect to q, k and v
  *
  * Tensors (all row-major, contiguous, head_dim innermost):
  *   q      [B, H,    N, d]          I/O dtype
@@ -73,7 +74,7 @@ typedef enum {
 typedef enum { PSA_F32 = 0, PSA_BF16 = 1 } psa_dtype_t;
 
 /* Which call a workspace size is asked for. */
-typedef enum { PSA_WS_ESTIMATE_MASK = 0, PSA_WS_ATTENTION_FWD = 1 } psa_workspace_kind_t;
+typedef enum { PSA_WS_ESTIMATE_MASK = 0, PSA_WS_ATTENTION_FWD = 1, PSA_WS_ATTENTION_BWD = 2 } psa_workspace_kind_t;
 
 typedef struct {
   int32_t B, H, H_kv, N, d;   /* d in {64, 128}; H % H_kv == 0; B * H <= 65535        */
@@ -202,6 +203,32 @@ psa_status_t psa_estimate_mask_ranked(const psa_problem_t* prob, const void* q, 
 psa_status_t psa_attention_fwd(const psa_problem_t* prob, const void* q, const void* k,
                                const void* v, const void* k_pyr, const void* v_pyr,
                                const int8_t* level_map, void* o, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward of step 3: gradients of the attention output with respect to q, k and v,
+ * with the level map held fixed (it is a discrete choice). The pages describe no
+ * backward pass; they imply training use (the top168.com article's models are
+ * fine-tuned and distilled with PSA), and this is the exact gradient of the forward
+ * defined by psa_attention_fwd. With P_rp = e^{a_rp - lse_r} over the pooled keys p of
+ * row r (the causal rule applied as in the forward) and D_r = <dO_r, O_r>:
+ *   dV_p = sum_r P_rp dO_r,  dA_rp = P_rp (<dO_r, V_p> - D_r),
+ *   dq_r = scale sum_p dA_rp K_p,  dK_p = scale sum_r dA_rp q_r,
+ * and a pooled row, the mean of its c tokens, passes 1/c of its gradient to each;
+ * dk and dv sum over the query heads that share the KV head.
+ * Inputs: q, k, v, k_pyr, v_pyr, level_map as given to psa_attention_fwd, and that
+ * call's outputs o (I/O dtype) and lse (float32, required), d_o = dL/dO like o.
+ * Outputs dq like q, dk and dv like k (I/O dtype), every element written.
+ * workspace: psa_workspace_bytes(prob, PSA_WS_ATTENTION_BWD) bytes of device memory,
+ * 16-byte aligned, contents on entry irrelevant (row dots, then float32 per-level
+ * gradients of K and of V). Arithmetic: bf16 operands on the matrix cores with
+ * float32 accumulation (P and dA rounded to bf16 for their products), like the
+ * forward.
+ */
+psa_status_t psa_attention_bwd(const psa_problem_t* prob, const void* q, const void* k, const void* v,
+                               const void* k_pyr, const void* v_pyr, const int8_t* level_map,
+                               const void* o, const float* lse, const void* d_o,
+                               void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a status code ("PSA_OK", ...); never NULL. */

@@ -28,12 +28,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 PSA_OK, PSA_ERR_INVALID_ARGUMENT, PSA_ERR_UNSUPPORTED, PSA_ERR_WORKSPACE_TOO_SMALL, PSA_ERR_HIP = range(5)
 PSA_F32, PSA_BF16 = 0, 1
-PSA_WS_ESTIMATE_MASK, PSA_WS_ATTENTION_FWD = 0, 1
+PSA_WS_ESTIMATE_MASK, PSA_WS_ATTENTION_FWD, PSA_WS_ATTENTION_BWD = 0, 1, 2
 
 EXPORTED = (
     "psa_pyramid_rows", "psa_workspace_bytes", "psa_check_problem", "psa_build_pyramid", "psa_build_pyramid_sim",
     "psa_apply_similarity_cap",
-    "psa_estimate_mask", "psa_estimate_mask_ranked", "psa_attention_fwd", "psa_status_string", "psa_last_error",
+    "psa_estimate_mask", "psa_estimate_mask_ranked", "psa_attention_fwd", "psa_attention_bwd", "psa_status_string", "psa_last_error",
 )
 
 
@@ -63,6 +63,8 @@ _lib.psa_estimate_mask.restype = _st
 _lib.psa_estimate_mask_ranked.argtypes = [_P, _vp, _vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int32, _vp,
                                           _vp, _vp, _sz, _vp]
 _lib.psa_estimate_mask_ranked.restype = _st
+_lib.psa_attention_bwd.argtypes = [_P] + [_vp] * 13 + [_sz, _vp]
+_lib.psa_attention_bwd.restype = _st
 _lib.psa_attention_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.psa_attention_fwd.restype = _st
 _lib.psa_status_string.argtypes, _lib.psa_status_string.restype = [_st], ctypes.c_char_p
@@ -261,6 +263,38 @@ def psa_attention_fwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.
     _check(_lib.psa_attention_fwd(ctypes.byref(prob.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(k_pyr), _ptr(v_pyr),
                                   _ptr(level_map), _ptr(o), _ptr(lse), None, 0, _stream(stream)))
     return o, lse
+
+
+def psa_attention_bwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      k_pyr: Optional[torch.Tensor], v_pyr: Optional[torch.Tensor], level_map: torch.Tensor,
+                      o: torch.Tensor, lse: torch.Tensor, d_o: torch.Tensor, dq: Optional[torch.Tensor] = None,
+                      dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of step 3 with the level map fixed: returns (dq, dk, dv)."""
+    dt = prob.torch_dtype
+    q_shape = (prob.B, prob.H, prob.N, prob.d)
+    kv_shape = (prob.B, prob.H_kv, prob.N, prob.d)
+    for t, name, shape in ((q, "q", q_shape), (k, "k", kv_shape), (v, "v", kv_shape), (o, "o", q_shape),
+                           (d_o, "d_o", q_shape)):
+        _need(t, name, shape, dt)
+    _need(lse, "lse", (prob.B, prob.H, prob.N), torch.float32)
+    _need(level_map, "level_map", (prob.B, prob.H, prob.nqb, prob.nkb), torch.int8)
+    if prob.num_levels > 1:
+        for t, name in ((k_pyr, "k_pyr"), (v_pyr, "v_pyr")):
+            _need(t, name, (prob.B, prob.H_kv, prob.pyramid_rows, prob.d), dt)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q_shape, dt)
+    _need(dk, "dk", kv_shape, dt)
+    _need(dv, "dv", kv_shape, dt)
+    ws_bytes = prob.workspace_bytes(PSA_WS_ATTENTION_BWD)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _check(_lib.psa_attention_bwd(ctypes.byref(prob.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(k_pyr), _ptr(v_pyr),
+                                  _ptr(level_map), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
 
 
 def psa_forward(prob: Problem, q, k, v, thresholds, n_dense_prefix: int = 0, stream=None):

@@ -118,9 +118,19 @@ size_t psa_pyramid_rows(const psa_problem_t* prob) {
   return (size_t)pyramid_rows(prob);
 }
 
+// Backward workspace: row dots D [B, H, N], then the float32 per-level gradients of K and
+// of V [B, H_kv, N + pyramid rows, d]; each part starts on a 256-byte boundary.
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t bwd_dr_bytes(const psa_problem_t* p) { return round256((size_t)p->B * p->H * p->N * sizeof(float)); }
+size_t bwd_grad_bytes(const psa_problem_t* p) {
+  return round256((size_t)p->B * p->H_kv * (p->N + pyramid_rows(p)) * p->d * sizeof(float));
+}
+size_t bwd_workspace(const psa_problem_t* p) { return bwd_dr_bytes(p) + 2 * bwd_grad_bytes(p); }
+
 size_t psa_workspace_bytes(const psa_problem_t* prob, psa_workspace_kind_t kind) {
   if (check_problem(prob) != PSA_OK) return 0;
   if (kind == PSA_WS_ESTIMATE_MASK) return mask_workspace(prob);
+  if (kind == PSA_WS_ATTENTION_BWD) return bwd_workspace(prob);
   return 0;
 }
 
@@ -297,6 +307,51 @@ psa_status_t psa_attention_fwd(const psa_problem_t* prob, const void* q, const v
   a.pyr_rows = pyramid_rows(prob);
   level_offsets(prob, a.off, a.rows);
   return hip_status(psa::launch_attention(a, stream), "psa_attention_fwd launch");
+}
+
+psa_status_t psa_attention_bwd(const psa_problem_t* prob, const void* q, const void* k, const void* v,
+                               const void* k_pyr, const void* v_pyr, const int8_t* level_map, const void* o,
+                               const float* lse, const void* d_o, void* dq, void* dk, void* dv, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  psa_status_t s = check_problem(prob);
+  if (s != PSA_OK) return s;
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(level_map, "level_map");
+  REQUIRE_PTR(o, "o");
+  REQUIRE_PTR(lse, "lse");
+  REQUIRE_PTR(d_o, "d_o");
+  REQUIRE_PTR(dq, "dq");
+  REQUIRE_PTR(dk, "dk");
+  REQUIRE_PTR(dv, "dv");
+  if (prob->num_levels > 1) {
+    REQUIRE_PTR(k_pyr, "k_pyr");
+    REQUIRE_PTR(v_pyr, "v_pyr");
+  }
+  const size_t need = bwd_workspace(prob);
+  if (workspace_bytes < need)
+    return fail(PSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  REQUIRE_PTR(workspace, "workspace");
+  psa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.k_pyr = k_pyr; a.v_pyr = v_pyr; a.level_map = level_map;
+  a.o = o; a.lse = lse; a.dout = d_o; a.dq = dq; a.dk = dk; a.dv = dv;
+  char* ws = static_cast<char*>(workspace);
+  a.Dr = reinterpret_cast<float*>(ws);
+  a.dkw = reinterpret_cast<float*>(ws + bwd_dr_bytes(prob));
+  a.dvw = reinterpret_cast<float*>(ws + bwd_dr_bytes(prob) + bwd_grad_bytes(prob));
+  a.B = prob->B; a.H = prob->H; a.H_kv = prob->H_kv; a.N = prob->N; a.d = prob->d;
+  a.q_block = prob->q_block;
+  a.nqb = (int)ceil_div(prob->N, prob->q_block);
+  a.nkb = (int)ceil_div(prob->N, psa::kKvBlock);
+  a.L = prob->num_levels;
+  a.bf16 = prob->dtype == PSA_BF16;
+  a.causal = prob->causal != 0;
+  a.scale = effective_scale(prob);
+  a.pyr_rows = pyramid_rows(prob);
+  level_offsets(prob, a.off, a.rows);
+  return hip_status(psa::launch_attention_bwd(a, stream), "psa_attention_bwd launch");
 }
 
 const char* psa_status_string(psa_status_t status) {

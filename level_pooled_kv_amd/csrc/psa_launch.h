@@ -53,7 +53,23 @@ struct CapArgs {
   int B, H, H_kv, nqb, nkb, L;
 };
 
+struct BwdArgs {
+  const void* q; const void* k; const void* v; const void* k_pyr; const void* v_pyr;
+  const int8_t* level_map; const void* o; const float* lse; const void* dout;
+  void* dq; void* dk; void* dv;
+  float* Dr;                     // workspace: [B, H, N] row dots <dO, O>
+  float* dkw; float* dvw;        // workspace: [B, H_kv, N + pyr_rows, d] float32 per-level pooled gradients
+  int B, H, H_kv, N, d, q_block, nqb, nkb, L;
+  bool bf16;
+  bool causal;
+  float scale;
+  int64_t pyr_rows;
+  int off[kMaxLevels];           // row offset of level l (l >= 1) in the pyramid
+  int rows[kMaxLevels];          // ceil(N / 2^l)
+};
+
 hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t stream);
+hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_similarity_cap(const CapArgs& a, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
 int mask_score_stride(int nkb);  // padded row length of the score workspace

@@ -1,0 +1,166 @@
+"""Parity of the attention backward (psa_attention_bwd, through the C ABI) with the
+float64 oracle on MI355X.
+
+Tolerance (derived, not fitted): the kernels round P and dA to bf16 for their matrix
+products (relative 2^-9 per element) and take D_r = <dO_r, O_r> from the bf16 output,
+so each gradient carries relative errors of about 2^-9 per term; summed with random
+signs that stays near 2^-9 of the gradient's L2 norm. The bar is 1e-2 of the L2 norm
+(bf16 I/O) and 2e-2 for float32 I/O, whose inputs are also rounded to bf16 on the way
+into the matrix cores, plus a max-abs bound of 5e-2 of the largest reference entry.
+Every case prints its name before touching the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import psa_oracle as o
+from synth import generate, get as get_workload, random_qkv
+from tests.psa_check import to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+REL = {"bf16": 1e-2, "f32": 2e-2}
+MAXREL = 5e-2
+
+
+@pytest.fixture(scope="module")
+def psa():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import level_pooled_kv_amd as lib
+    return lib
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def check_grad(g, r, dtype, label):
+    assert np.all(np.isfinite(g)), (label, "non-finite gradient")
+    nr = np.linalg.norm(r.ravel())
+    if nr == 0.0:   # e.g. a single key: dA = P (dP - D) vanishes up to float32 arithmetic
+        assert np.abs(g).max() <= 1e-5, (label, "expected a zero gradient", float(np.abs(g).max()))
+        return 0.0
+    rel = np.linalg.norm((g - r).ravel()) / nr
+    mx = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
+    assert rel <= REL[dtype] and mx <= MAXREL, (label, float(rel), float(mx))
+    return float(rel)
+
+
+def run_bwd(psa, label, q, k, v, lev, *, H, H_kv, d, q_block, L, dtype, causal=False, seed=0):
+    B, _, N, _ = q.shape
+    s = 1.0 / math.sqrt(d)
+    prob = psa.Problem(B=B, H=H, H_kv=H_kv, N=N, d=d, q_block=q_block, num_levels=L, dtype=dtype, causal=causal)
+    dO = np.random.default_rng(seed).standard_normal(q.shape)
+    if dtype == "bf16":
+        dO = o.round_to_bf16(dO)
+    say(f"{label}: backward B={B} H={H} H_kv={H_kv} N={N} d={d} q_block={q_block} L={L} {dtype} causal={causal}")
+    qd, kd, vd, dod = to_device(q, dtype), to_device(k, dtype), to_device(v, dtype), to_device(dO, dtype)
+    kp, vp, _ = psa.psa_build_pyramid(prob, kd, vd)
+    lev_d = torch.from_numpy(lev).cuda()
+    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lev_d, want_lse=True)
+    dq, dk, dv = psa.psa_attention_bwd(prob, qd, kd, vd, kp, vp, lev_d, out, lse, dod)
+    torch.cuda.synchronize()
+    ref = o.pyramid_attention_bwd(q, k, v, L, lev, q_block, 64, s, dO, io_dtype=dtype, causal=causal)
+    rels = [check_grad(to_host(x), ref[n], dtype, f"{label} {n}") for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    say(f"{label}: ok (relative L2 error dq {rels[0]:.1e} dk {rels[1]:.1e} dv {rels[2]:.1e})")
+    return ref
+
+
+CASES = [
+    # label, N, d, q_block, L, dtype, H, H_kv, causal
+    ("tiny shape f32 bq64", 2048, 64, 64, 4, "f32", 2, 2, False),
+    ("ragged N=2045 d128 bq128 gqa", 2045, 128, 128, 4, "bf16", 4, 2, False),
+    ("N=130 d64 bq64", 130, 64, 64, 4, "bf16", 2, 2, False),
+    ("N=1 d128", 1, 128, 128, 4, "bf16", 1, 1, False),
+    ("N=1536 d128 L=1", 1536, 128, 128, 1, "bf16", 2, 2, False),
+    ("N=900 d128 f32 L=3", 900, 128, 128, 3, "f32", 2, 1, False),
+    ("causal N=1000 d128 bq128", 1000, 128, 128, 4, "bf16", 2, 2, True),
+    ("causal N=777 d64 bq64 f32", 777, 64, 64, 4, "f32", 2, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_on_mask(psa, case):
+    label, N, d, bq, L, dtype, H, H_kv, causal = case
+    q, k, v = random_qkv(N + 11 * d + L, 1, H, H_kv, N, d, dtype)
+    tau = (0.3, 0.55, 0.75, 0.9)[:L]
+    lev = o.estimate_mask(q, k, bq, 64, tau, L, 1 / math.sqrt(d), causal=causal)["levels"]
+    run_bwd(psa, label, q, k, v, lev, H=H, H_kv=H_kv, d=d, q_block=bq, L=L, dtype=dtype, causal=causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_arbitrary_maps(psa, causal):
+    # every level anywhere (pooled blocks on the diagonal, rows that keep nothing)
+    N, d, bq, H, H_kv = 1100, 128, 128, 2, 2
+    q, k, v = random_qkv(N + 23, 1, H, H_kv, N, d, "bf16")
+    nqb, nkb = -(-N // bq), -(-N // 64)
+    lev = np.random.default_rng(5).integers(-1, 4, size=(1, H, nqb, nkb)).astype(np.int8)
+    lev[0, 1, 2] = -1                                   # a query block that keeps nothing
+    ref = run_bwd(psa, f"arbitrary maps causal={causal}", q, k, v, lev, H=H, H_kv=H_kv, d=d, q_block=bq, L=4,
+                  dtype="bf16", causal=causal)
+    assert np.all(ref["dq"][0, 1, 256:384] == 0)
+
+
+def test_backward_dense_map_equals_dense_gradient(psa):
+    N, d = 1000, 64
+    q, k, v = random_qkv(41, 1, 2, 2, N, d, "bf16")
+    lev = np.zeros((1, 2, 8, 16), dtype=np.int8)
+    ref = run_bwd(psa, "dense map", q, k, v, lev, H=2, H_kv=2, d=d, q_block=128, L=1, dtype="bf16")
+    qt, kt, vt = (torch.tensor(np.asarray(x, np.float64), requires_grad=True) for x in (q, k, v))
+    dO = np.random.default_rng(0).standard_normal(q.shape)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=1 / math.sqrt(d))
+    out.backward(torch.from_numpy(o.round_to_bf16(dO)).double())
+    np.testing.assert_allclose(ref["dq"], qt.grad.numpy(), rtol=0, atol=1e-9)
+
+
+def test_backward_full_workload_sampled(psa):
+    # wan13b at full size: dq on sampled query blocks, dk and dv on sampled KV blocks
+    w = get_workload("wan13b")
+    L, s = w.num_levels, w.scale
+    say(f"{w.name}: backward at full size, generating inputs")
+    q, k, v = generate(w, "q"), generate(w, "k"), generate(w, "v")
+    dO = o.round_to_bf16(np.random.default_rng(9).standard_normal(q.shape).astype(np.float32))
+    prob = psa.Problem(B=w.B, H=w.H, H_kv=w.H_kv, N=w.N, d=w.d, q_block=w.q_block, num_levels=L, dtype=w.dtype)
+    qd, kd, vd, dod = (to_device(x, w.dtype) for x in (q, k, v, dO))
+    kp, vp, kbar = psa.psa_build_pyramid(prob, kd, vd)
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, w.thresholds())
+    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lev, want_lse=True)
+    say(f"{w.name}: GPU backward")
+    dq, dk, dv = psa.psa_attention_bwd(prob, qd, kd, vd, kp, vp, lev, out, lse, dod)
+    torch.cuda.synchronize()
+    lev_h = lev.cpu().numpy()
+    dq_g, dk_g, dv_g = to_host(dq), to_host(dk), to_host(dv)
+    say(f"{w.name}: oracle on sampled blocks")
+    pyr = {}
+    for name, x in (("k", k), ("v", v)):
+        for g in (0, 5):
+            pyr[(name, g)] = [x[:, g:g + 1].astype(np.float64)] + \
+                [o.round_to_io(a, w.dtype) for a in o.build_pyramid(x[:, g:g + 1], L)[1:]]
+    # dq of sampled query blocks of heads 0 and 5: the oracle's backward restricted to one query block
+    for h, i in ((0, 0), (0, 131), (5, 255), (5, 77)):
+        r0, r1 = i * w.q_block, min((i + 1) * w.q_block, w.N)
+        sub = lev_h[:, h:h + 1, i:i + 1]
+        qs = np.zeros((1, 1, w.N, w.d))
+        qs[:, :, r0:r1] = q[:, h:h + 1, r0:r1]
+        dOs = np.zeros((1, 1, w.N, w.d))
+        dOs[:, :, r0:r1] = dO[:, h:h + 1, r0:r1]
+        levs = np.full((1, 1, w.nqb, w.nkb), -1, dtype=np.int8)
+        levs[:, :, i] = sub[:, :, 0]
+        ref = o.pyramid_attention_bwd(qs, k[:, h:h + 1], v[:, h:h + 1], L, levs, w.q_block, 64, s, dOs,
+                                      io_dtype=w.dtype)
+        check_grad(dq_g[:, h:h + 1, r0:r1], ref["dq"][:, :, r0:r1], w.dtype, f"dq head {h} block {i}")
+    # dk, dv of sampled KV blocks: every query block of the head that keeps the block contributes
+    for h, j in ((0, 3), (5, 400)):
+        rows = [i for i in range(w.nqb) if lev_h[0, h, i, j] >= 0]
+        levs = np.full((1, 1, w.nqb, w.nkb), -1, dtype=np.int8)
+        levs[0, 0, rows] = lev_h[0, h, rows]
+        ref = o.pyramid_attention_bwd(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], L, levs, w.q_block, 64, s,
+                                      dO[:, h:h + 1], io_dtype=w.dtype)
+        t0, t1 = 64 * j, 64 * j + 64
+        # only block j's own tokens are compared: other blocks also get contributions from
+        # query blocks outside the sample
+        check_grad(dk_g[:, h:h + 1, t0:t1], ref["dk"][:, :, t0:t1], w.dtype, f"dk head {h} block {j}")
+        check_grad(dv_g[:, h:h + 1, t0:t1], ref["dv"][:, :, t0:t1], w.dtype, f"dv head {h} block {j}")
+    say(f"{w.name}: ok")
