@@ -199,6 +199,8 @@ def main():
     ap.add_argument("--similarity", type=float, default=None, metavar="THRESHOLD",
                     help="add the cosine-similarity constraint: the pyramid step also computes the key "
                          "similarity and the level map is capped at THRESHOLD before attention")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time psa_attention_bwd on the step's output and report it under 'backward'")
     ap.add_argument("--compare-rules", action="store_true",
                     help="only compare the output error of threshold / ranked / binary masks at equal "
                          "FLOP fraction against dense attention, print that JSON line and exit")
@@ -284,6 +286,24 @@ def main():
     per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])   # ms
     pyr_ms, mask_ms, attn_ms = (float(np.mean(per[:, i])) for i in range(3))
 
+    bwd = None
+    if args.backward:
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        psa.psa_attention_fwd(prob, qd, kd, vd, k_pyr, v_pyr, level_map, o=o, lse=lse)
+        d_o = torch.randn(qd.shape, generator=torch.Generator(device=dev).manual_seed(7), device=dev).to(dt)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        bws = torch.empty(prob.workspace_bytes(psa.PSA_WS_ATTENTION_BWD), dtype=torch.uint8, device=dev)
+        for _ in range(max(args.warmup, 1)):
+            psa.psa_attention_bwd(prob, qd, kd, vd, k_pyr, v_pyr, level_map, o, lse, d_o, dq, dk, dv, workspace=bws)
+        torch.cuda.synchronize()
+        bev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        bev[0].record()
+        for s_ in range(args.steps):
+            psa.psa_attention_bwd(prob, qd, kd, vd, k_pyr, v_pyr, level_map, o, lse, d_o, dq, dk, dv, workspace=bws)
+            bev[s_ + 1].record()
+        torch.cuda.synchronize()
+        bwd = float(np.mean([bev[i].elapsed_time(bev[i + 1]) for i in range(args.steps)]))
+
     lm = level_map.cpu().numpy()
     flops = effective_flops(lm, w.N, w.q_block, w.kv_block, w.d, causal=w.causal)
     rho = flops / w.dense_flops()
@@ -321,6 +341,14 @@ def main():
                 "build_pyramid_bytes": pyr_bytes, "estimate_mask_bytes": mask_bytes},
         "levels": level_histogram(lm),
     }
+    if bwd is not None:
+        # algorithmic backward work: the five products of an attention backward (S and dP
+        # recomputed once, dq, dK, dV), 2.5 x the forward's two
+        bflops = 2.5 * flops
+        result["backward"] = {"ms_per_call": round(bwd, 4), "effective_flops": bflops,
+                              "achieved_tflops": round(bflops / (bwd * 1e-3) / 1e12, 2),
+                              "frac_of_peak": round(bflops / (bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "call": "psa_attention_bwd (row dots, dq, dK/dV, unpool)"}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a head sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, tau, fractions)

@@ -196,12 +196,14 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
     const float lvlf = (float)ti.lvl;
     const uint16_t* Kb = kbuf(P);
     const uint16_t* Vb = vbuf(P);
+    int zero;   // opaque: keeps the LDS address arithmetic in the loop (hoisted, it spilled)
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 sacc, dpacc;
 #pragma unroll
       for (int x = 0; x < 16; ++x) sacc[x] = dpacc[x] = 0.f;
-      const int krow = 32 * kb + l32;
+      const int krow = 32 * kb + l32 + zero;
       const uint16_t* kr = Kb + krow * D;
       const uint16_t* vr = Vb + krow * D;
       const int swz = k_swz<D>(krow);
@@ -243,7 +245,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
           bf16x4 part[2];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const int row = 16 * c + 8 * j + tr_row;
+            const int row = 16 * c + 8 * j + tr_row + zero;
             const int col = 32 * tt + tr_col;
             const int chunk = (col >> 3) ^ k_swz<D>(row);
             part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Kb + row * D + chunk * 8 + (col & 7)));
@@ -399,29 +401,51 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
       const int hh = pair / nqb, i = pair - hh * nqb;
       const int64_t bh = (int64_t)b * H + g * G + hh;
       const int key_used = (mask >> (krow >> sh)) & 1;
+      // this wave's 32 keys: segments (32 kh) >> sh .. (32 kh + 31) >> sh
+      const uint32_t hmask = lvl == 0 ? 1u : ((1u << (nseg >> 1)) - 1u) << (kh * (nseg >> 1));
+      const bool active = (mask & hmask) != 0;   // wave-uniform: nothing to add otherwise
       const float keyb = s_keyb[krow];
       const int ktok = s_ltok[krow];
       for (int r0 = i * q_block; r0 < min((i + 1) * q_block, N); r0 += 64) {
         __syncthreads();                      // the previous chunk's reads are done
-        for (int u = tid; u < 64 * CH; u += 256) {
-          const int row = u / CH, ch = u - row * CH;
-          const int r = r0 + row;
-          U128 qq{{0u, 0u, 0u, 0u}}, dd{{0u, 0u, 0u, 0u}};
-          if (r < N) {
-            if constexpr (sizeof(T) == 2) {
-              qq = ld128(q + (bh * N + r) * D + ch * 8);
-              dd = ld128(dout + (bh * N + r) * D + ch * 8);
-            } else {
-              Raw8f rq, rd;
-              rq.load(reinterpret_cast<const float*>(q) + (bh * N + r) * D + ch * 8);
-              rd.load(reinterpret_cast<const float*>(dout) + (bh * N + r) * D + ch * 8);
-              qq = rq.bf16();
-              dd = rd.bf16();
+        // stage Q and dO rows r0..r0+63 (K swizzle; rows past N read row N-1 and are
+        // never used: their lse2 is +inf, so P = dS = 0). bf16: direct global -> LDS
+        // loads, each wave filling 1 KB blocks of RPK rows; all loads issued before any wait.
+        {
+          constexpr int RPK = 1024 / (2 * D);        // rows per 1 KB block
+          constexpr int NBLK = 64 / RPK;             // blocks per tensor
+          constexpr int BPWV = NBLK / 4;             // blocks per wave and tensor
+          const int lrow = lane / CH, lch = lane % CH;
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int bb = 0; bb < BPWV; ++bb) {
+              const int blk = wave * BPWV + bb;
+              const int row = blk * RPK + lrow;
+              const int64_t r = min(r0 + row, N - 1);
+              const int lc = lch ^ k_swz<D>(row);     // logical chunk stored in physical slot lch
+              __builtin_amdgcn_global_load_lds((gbl_void*)(q + (bh * N + r) * D + lc * 8), (lds_void*)(Qs + blk * 512),
+                                               16, 0, 0);
+              __builtin_amdgcn_global_load_lds((gbl_void*)(dout + (bh * N + r) * D + lc * 8),
+                                               (lds_void*)(Os + blk * 512), 16, 0, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+          } else {
+            Raw8f rq[BPWV], rd[BPWV];
+#pragma unroll
+            for (int bb = 0; bb < BPWV; ++bb) {
+              const int row = (wave * BPWV + bb) * RPK + lrow;
+              const int64_t r = min(r0 + row, N - 1);
+              const int lc = lch ^ k_swz<D>(row);
+              rq[bb].load(reinterpret_cast<const float*>(q) + (bh * N + r) * D + lc * 8);
+              rd[bb].load(reinterpret_cast<const float*>(dout) + (bh * N + r) * D + lc * 8);
+            }
+#pragma unroll
+            for (int bb = 0; bb < BPWV; ++bb) {
+              const int blk = wave * BPWV + bb;
+              st128(Qs + blk * 512 + lane * 8, rq[bb].bf16());
+              st128(Os + blk * 512 + lane * 8, rd[bb].bf16());
             }
           }
-          const int pc = ch ^ k_swz<D>(row);
-          st128(Qs + row * D + pc * 8, qq);
-          st128(Os + row * D + pc * 8, dd);
         }
         if (tid < 64) {
           const int r = r0 + tid;
@@ -431,6 +455,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
         }
         __syncthreads();
 
+        if (!active) continue;                // the loop's barrier is at its top: no wave skips one
         // S = Q K^T and dP = dO V^T for 32 queries x 32 keys: lane holds key column krow,
         // rows = queries 32qh + 8(x>>2) + 4half + (x&3)
         f32x16 sacc, dpacc;
