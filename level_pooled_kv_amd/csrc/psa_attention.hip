@@ -140,6 +140,18 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   Raw8f fk[kDirect ? 1 : BPW], fv[kDirect ? 1 : BPW];
   auto kbuf = [&](auto P) -> uint16_t* { if constexpr (P() == 0) return K0; else return K1; };
   auto vbuf = [&](auto P) -> uint16_t* { if constexpr (P() == 0) return V0; else return V1; };
+  // Per-key fixups of a tile that needs them (rare: the last tile of a level, or a
+  // causal diagonal tile), kept out of the common path: logit corrections of padding and
+  // ragged pooled rows, and the last token of each staged key row.
+  auto tile_fixups = [&](const TileInfo& ti, int buf, const int* fprow, const bool* fok) {
+    if (st_pchunk != 0) return;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int row = st_row0 + RPB * i;
+      if (ti.irr) corr[buf][row] = key_correction(fok[i], ti.lvl, fprow[i], N, cs);
+      if (ti.diag) ltok[buf][row] = key_last_token(fok[i], ti.lvl, fprow[i], N);
+    }
+  };
   auto issue_tile = [&](int t, auto P) {
     constexpr int buf = P();
     const TileInfo ti = tile_info(t);
@@ -150,6 +162,8 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     // wave-uniform bases of the level + 32-bit per-lane byte offsets (scalar-base addressing)
     const char* kb = reinterpret_cast<const char*>(lvl == 0 ? kh : kph + loff);
     const char* vb = reinterpret_cast<const char*>(lvl == 0 ? vh : vph + loff);
+    int fx_prow[BPW];
+    bool fx_ok[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int row = st_row0 + RPB * i;
@@ -169,9 +183,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         fk[i].load(reinterpret_cast<const float*>(kb + koff));
         fv[i].load(reinterpret_cast<const float*>(vb + voff));
       }
-      if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
-      if (ti.diag && st_pchunk == 0) ltok[buf][row] = key_last_token(ok, lvl, prow, N);
+      fx_prow[i] = prow;
+      fx_ok[i] = ok;
     }
+    if (__builtin_expect(ti.irr || ti.diag, 0)) tile_fixups(ti, buf, fx_prow, fx_ok);
   };
   // Direct-load path: the byte offsets of tile t's staged rows are computed up front
   // (with the tile's logit corrections when irregular), and the loads themselves are
@@ -188,6 +203,8 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const int64_t loff = (int64_t)level_off(lvl) * D;
     st.kb = reinterpret_cast<const char*>(lvl == 0 ? kh : kph + loff);
     st.vb = reinterpret_cast<const char*>(lvl == 0 ? vh : vph + loff);
+    int fx_prow[BPW];
+    bool fx_ok[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int row = st_row0 + RPB * i;
@@ -199,9 +216,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       const int rowel = (ok ? prow : 0) * D;
       st.koff[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ k_swz<D>(row))) * (int)sizeof(T));
       st.voff[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ v_swz<D>(row))) * (int)sizeof(T));
-      if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
-      if (ti.diag && st_pchunk == 0) ltok[buf][row] = key_last_token(ok, lvl, prow, N);
+      fx_prow[i] = prow;
+      fx_ok[i] = ok;
     }
+    if (__builtin_expect(ti.irr || ti.diag, 0)) tile_fixups(ti, buf, fx_prow, fx_ok);
     return st;
   };
   auto dma_k = [&](const Stage& st, int i, auto P) {

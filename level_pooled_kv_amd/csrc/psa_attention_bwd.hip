@@ -125,6 +125,17 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
   Raw8f fk[kDirect ? 1 : BPW], fv[kDirect ? 1 : BPW];
   auto kbuf = [&](auto P) -> uint16_t* { if constexpr (P() == 0) return K0; else return K1; };
   auto vbuf = [&](auto P) -> uint16_t* { if constexpr (P() == 0) return V0; else return V1; };
+  // Per-key fixups of the rare tiles that need them (last of a level, causal diagonal),
+  // out of the common path: logit corrections and last tokens of the staged key rows.
+  auto tile_fixups = [&](const TileInfo& ti, int buf, const int* fprow, const bool* fok) {
+    if (st_pchunk != 0) return;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int row = st_row0 + RPB * i;
+      if (ti.irr) corr[buf][row] = key_correction(fok[i], ti.lvl, fprow[i], N, cs);
+      if (ti.diag) ltok[buf][row] = key_last_token(fok[i], ti.lvl, fprow[i], N);
+    }
+  };
   // Both K and V are read row-wise (A operands) and K also transposed; both tiles use
   // the K swizzle.
   auto issue_tile = [&](int t, auto P) {
@@ -136,6 +147,8 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
     const int64_t loff = (int64_t)level_off(lvl) * D;
     const char* kb = reinterpret_cast<const char*>(lvl == 0 ? kh : kph + loff);
     const char* vb = reinterpret_cast<const char*>(lvl == 0 ? vh : vph + loff);
+    int fx_prow[BPW];
+    bool fx_ok[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
       const int row = st_row0 + RPB * i;
@@ -154,9 +167,10 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
         fk[i].load(reinterpret_cast<const float*>(kb + off));
         fv[i].load(reinterpret_cast<const float*>(vb + off));
       }
-      if (ti.irr && st_pchunk == 0) corr[buf][row] = key_correction(ok, lvl, prow, N, cs);
-      if (ti.diag && st_pchunk == 0) ltok[buf][row] = key_last_token(ok, lvl, prow, N);
+      fx_prow[i] = prow;
+      fx_ok[i] = ok;
     }
+    if (__builtin_expect(ti.irr || ti.diag, 0)) tile_fixups(ti, buf, fx_prow, fx_ok);
   };
   auto commit_tile = [&](auto P) {
     if constexpr (!kDirect) {
