@@ -220,8 +220,8 @@ psa_status_t psa_attention_fwd(const psa_problem_t* prob, const void* q, const v
  * call's outputs o (I/O dtype) and lse (float32, required), d_o = dL/dO like o.
  * Outputs dq like q, dk and dv like k (I/O dtype), every element written.
  * workspace: psa_workspace_bytes(prob, PSA_WS_ATTENTION_BWD) bytes of device memory,
- * 16-byte aligned, contents on entry irrelevant (row dots, then float32 per-level
- * gradients of K and of V). Arithmetic: bf16 operands on the matrix cores with
+ * 16-byte aligned, contents on entry irrelevant (per query row the lse in base 2 and
+ * the row dot <dO, O>, then float32 per-level gradients of K and of V). Arithmetic: bf16 operands on the matrix cores with
  * float32 accumulation (P and dA rounded to bf16 for their products), like the
  * forward.
  */

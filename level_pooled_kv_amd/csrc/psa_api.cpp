@@ -118,14 +118,17 @@ size_t psa_pyramid_rows(const psa_problem_t* prob) {
   return (size_t)pyramid_rows(prob);
 }
 
-// Backward workspace: row dots D [B, H, N], then the float32 per-level gradients of K and
-// of V [B, H_kv, N + pyramid rows, d]; each part starts on a 256-byte boundary.
+// Backward workspace: per query row the lse in base 2 and the row dot D, each [B, H, Npad]
+// with N padded to a multiple of 64 (padding rows: lse +inf, D 0), then the float32
+// per-level gradients of K and of V [B, H_kv, N + pyramid rows, d]; each part starts on a
+// 256-byte boundary.
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-size_t bwd_dr_bytes(const psa_problem_t* p) { return round256((size_t)p->B * p->H * p->N * sizeof(float)); }
+int bwd_npad(const psa_problem_t* p) { return (int)ceil_div(p->N, 64) * 64; }
+size_t bwd_dr_bytes(const psa_problem_t* p) { return round256((size_t)p->B * p->H * bwd_npad(p) * sizeof(float)); }
 size_t bwd_grad_bytes(const psa_problem_t* p) {
   return round256((size_t)p->B * p->H_kv * (p->N + pyramid_rows(p)) * p->d * sizeof(float));
 }
-size_t bwd_workspace(const psa_problem_t* p) { return bwd_dr_bytes(p) + 2 * bwd_grad_bytes(p); }
+size_t bwd_workspace(const psa_problem_t* p) { return 2 * bwd_dr_bytes(p) + 2 * bwd_grad_bytes(p); }
 
 size_t psa_workspace_bytes(const psa_problem_t* prob, psa_workspace_kind_t kind) {
   if (check_problem(prob) != PSA_OK) return 0;
@@ -338,9 +341,11 @@ psa_status_t psa_attention_bwd(const psa_problem_t* prob, const void* q, const v
   a.q = q; a.k = k; a.v = v; a.k_pyr = k_pyr; a.v_pyr = v_pyr; a.level_map = level_map;
   a.o = o; a.lse = lse; a.dout = d_o; a.dq = dq; a.dk = dk; a.dv = dv;
   char* ws = static_cast<char*>(workspace);
-  a.Dr = reinterpret_cast<float*>(ws);
-  a.dkw = reinterpret_cast<float*>(ws + bwd_dr_bytes(prob));
-  a.dvw = reinterpret_cast<float*>(ws + bwd_dr_bytes(prob) + bwd_grad_bytes(prob));
+  a.lse2 = reinterpret_cast<float*>(ws);
+  a.Dr = reinterpret_cast<float*>(ws + bwd_dr_bytes(prob));
+  a.dkw = reinterpret_cast<float*>(ws + 2 * bwd_dr_bytes(prob));
+  a.dvw = reinterpret_cast<float*>(ws + 2 * bwd_dr_bytes(prob) + bwd_grad_bytes(prob));
+  a.Npad = bwd_npad(prob);
   a.B = prob->B; a.H = prob->H; a.H_kv = prob->H_kv; a.N = prob->N; a.d = prob->d;
   a.q_block = prob->q_block;
   a.nqb = (int)ceil_div(prob->N, prob->q_block);

@@ -29,22 +29,34 @@
 namespace psa {
 
 // ------------------------------------------------------------------ D_r = <dO_r, O_r>
+// Row statistics of the backward, per (b, h) padded to Npad rows (a multiple of 64): the
+// lse in base 2 (+inf for a row that saw no key and for padding, so its P is 0) and D_r
+// (0 on padding).
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
-bwd_rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dout, float* __restrict__ Dr, int64_t rows) {
+bwd_rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
+                  float* __restrict__ lse2, float* __restrict__ Dr, int N, int Npad, int64_t rows) {
   constexpr int E = io_traits<T>::per16, CPR = D / E, RPB = 256 / CPR;
   const int t = threadIdx.x, lane = t & 63, chunk = t % CPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + t / CPR;
+  const int64_t prow = (int64_t)blockIdx.x * RPB + t / CPR;   // padded row index
+  const int64_t bh = prow / Npad;
+  const int r = (int)(prow - bh * Npad);
+  const bool live = prow < rows && r < N;
+  const int64_t row = bh * N + r;
   float s = 0.f;
-  if (row < rows) {
-    float a[E], b[E];
+  if (live) {
+    float a[E], c[E];
     unpack16<T>(ld128(o + row * D + chunk * E), a);
-    unpack16<T>(ld128(dout + row * D + chunk * E), b);
+    unpack16<T>(ld128(dout + row * D + chunk * E), c);
 #pragma unroll
-    for (int e = 0; e < E; ++e) s = fmaf(a[e], b[e], s);
+    for (int e = 0; e < E; ++e) s = fmaf(a[e], c[e], s);
   }
   s = group_sum<CPR>(s, lane);   // every lane takes part: no early exit above
-  if (row < rows && chunk == 0) Dr[row] = s;
+  if (prow < rows && chunk == 0) {
+    const float l = live ? lse[row] : -INFINITY;
+    lse2[prow] = l > -INFINITY ? l * 1.4426950408889634f : INFINITY;
+    Dr[prow] = s;
+  }
 }
 
 // ------------------------------------------------------------------ dq (query-outer)
@@ -54,7 +66,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
                            const T* __restrict__ kp, const T* __restrict__ vp,
                            const int8_t* __restrict__ level_map, const float* __restrict__ lse,
                            const float* __restrict__ Dr, const T* __restrict__ dout, T* __restrict__ dq,
-                           int H, int H_kv, int N, int nqb, int nkb, int L, int total_items, int per_xcd,
+                           int H, int H_kv, int N, int Npad, int nqb, int nkb, int L, int total_items, int per_xcd,
                            int64_t pyr_rows, int rows1, int rows2, float cs, float scale, int causal) {
   using C = AttnCfg<D, NW>;
   constexpr int CPR = C::kCpr, RPB = C::kRpb, BPW = C::kBpw;
@@ -107,7 +119,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
   const float lse_r = my_row < N ? lse[(int64_t)bh * N + my_row] : -INFINITY;
   const bool live = lse_r > -INFINITY;
   const float lse2 = live ? lse_r * 1.4426950408889634f : 0.f;
-  const float d_r = my_row < N ? Dr[(int64_t)bh * N + my_row] : 0.f;
+  const float d_r = my_row < N ? Dr[(int64_t)bh * Npad + my_row] : 0.f;
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
@@ -310,9 +322,9 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                              const T* __restrict__ kp, const T* __restrict__ vp,
-                             const int8_t* __restrict__ level_map, const float* __restrict__ lse,
-                             const float* __restrict__ Dr, const T* __restrict__ dout,
-                             float* __restrict__ dkw, float* __restrict__ dvw, int H, int H_kv, int N, int nqb,
+                             const int8_t* __restrict__ level_map, const float* __restrict__ lse2p,
+                             const float* __restrict__ Dp, const T* __restrict__ dout,
+                             float* __restrict__ dkw, float* __restrict__ dvw, int H, int H_kv, int N, int Npad, int nqb,
                              int nkb, int L, int q_block, int total_items, int per_xcd, int64_t pyr_rows,
                              int64_t rows_all, DkdvGeom geo, float cs, float scale, int causal) {
   static_assert(D == 64 || D == 128, "head dim");
@@ -326,7 +338,9 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
   uint16_t* Vs = pool + 64 * D;
   uint16_t* Qs = pool + 2 * 64 * D;
   uint16_t* Os = pool + 3 * 64 * D;
-  __shared__ float s_lse2[64], s_D[64], s_keyb[64];
+  __shared__ __align__(16) float s_lse2[64];
+  __shared__ __align__(16) float s_D[64];
+  __shared__ float s_keyb[64];
   __shared__ int s_ltok[64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -418,7 +432,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
       // this wave's 32 keys: segments (32 kh) >> sh .. (32 kh + 31) >> sh
       const uint32_t hmask = lvl == 0 ? 1u : ((1u << (nseg >> 1)) - 1u) << (kh * (nseg >> 1));
       const bool active = (mask & hmask) != 0;   // wave-uniform: nothing to add otherwise
-      const float keyb = s_keyb[krow];
+      const float kbias = key_used ? s_keyb[krow] : -INFINITY;   // log2 pool count; -inf: key not kept
       const int ktok = s_ltok[krow];
       for (int r0 = i * q_block; r0 < min((i + 1) * q_block, N); r0 += 64) {
         __syncthreads();                      // the previous chunk's reads are done
@@ -442,6 +456,10 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
               __builtin_amdgcn_global_load_lds((gbl_void*)(dout + (bh * N + r) * D + lc * 8),
                                                (lds_void*)(Os + blk * 512), 16, 0, 0);
             }
+            if (wave == 0)
+              __builtin_amdgcn_global_load_lds((gbl_void*)(lse2p + bh * Npad + r0 + lane), (lds_void*)s_lse2, 4, 0, 0);
+            if (wave == 1)
+              __builtin_amdgcn_global_load_lds((gbl_void*)(Dp + bh * Npad + r0 + lane), (lds_void*)s_D, 4, 0, 0);
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
           } else {
             Raw8f rq[BPWV], rd[BPWV];
@@ -461,11 +479,11 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
             }
           }
         }
-        if (tid < 64) {
-          const int r = r0 + tid;
-          const float lr = r < N ? lse[bh * N + r] : -INFINITY;
-          s_lse2[tid] = lr > -INFINITY ? lr * 1.4426950408889634f : INFINITY;   // no key: P = 0
-          s_D[tid] = r < N ? Dr[bh * N + r] : 0.f;
+        if constexpr (sizeof(T) != 2) {
+          if (tid < 64) {
+            s_lse2[tid] = lse2p[bh * Npad + r0 + tid];
+            s_D[tid] = Dp[bh * Npad + r0 + tid];
+          }
         }
         __syncthreads();
 
@@ -486,18 +504,22 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
           const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Vs + krow * D + (((2 * c + half) ^ kswz) * 8));
           dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dpacc, 0, 0, 0);
         }
+        // the 16 query rows of this lane's accumulator entries come in 4 runs of 4
         bf16x8 preg[2], dsreg[2];
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 lse4 = *reinterpret_cast<const float4*>(s_lse2 + 32 * qh + 8 * g4 + 4 * half);
+          const float4 dr4 = *reinterpret_cast<const float4*>(s_D + 32 * qh + 8 * g4 + 4 * half);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int x = 8 * cc + e;
-            const int ql = 32 * qh + 8 * (x >> 2) + 4 * half + (x & 3);   // query row in the chunk
-            bool seen = key_used != 0;
-            if (causal) seen = seen && ktok <= r0 + ql;
-            const float p = seen ? __builtin_amdgcn_exp2f(fmaf(sacc[x], cs, keyb - s_lse2[ql])) : 0.f;
-            preg[cc][e] = (__bf16)p;
-            dsreg[cc][e] = (__bf16)(p * (dpacc[x] - s_D[ql]));
+          for (int u = 0; u < 4; ++u) {
+            const int x = 4 * g4 + u;
+            const int ql = 32 * qh + 8 * g4 + 4 * half + u;   // query row in the chunk
+            // unseen pairs take an exponent of -inf (p = 0) instead of a branch
+            float arg = fmaf(sacc[x], cs, kbias - (&lse4.x)[u]);
+            if (causal) arg = ktok > r0 + ql ? -INFINITY : arg;
+            const float p = __builtin_amdgcn_exp2f(arg);
+            preg[x >> 3][x & 7] = (__bf16)p;
+            dsreg[x >> 3][x & 7] = (__bf16)(p * (dpacc[x] - (&dr4.x)[u]));
           }
         }
         // dV^T += dO^T P and dK^T += Q^T dS: A operands read transposed from LDS, the
@@ -624,10 +646,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const T* q = static_cast<const T*>(a.q);
   const T* o = static_cast<const T*>(a.o);
   const T* dout = static_cast<const T*>(a.dout);
-  const int64_t qrows = (int64_t)a.B * a.H * a.N;
+  const int64_t prows = (int64_t)a.B * a.H * a.Npad;
   const float cs = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3((unsigned)((qrows + 256 / CPR - 1) / (256 / CPR))), dim3(256), 0,
-                     stream, o, dout, a.Dr, qrows);
+  hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3((unsigned)((prows + 256 / CPR - 1) / (256 / CPR))), dim3(256), 0,
+                     stream, o, dout, a.lse, a.lse2, a.Dr, a.N, a.Npad, prows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -636,7 +658,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((pyramid_attn_bwd_dq_kernel<T, D, NW>), dim3(8 * per), dim3(NW * 64), 0, stream, q,
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.k_pyr),
                      static_cast<const T*>(a.v_pyr), a.level_map, a.lse, a.Dr, dout, static_cast<T*>(a.dq), a.H,
-                     a.H_kv, a.N, a.nqb, a.nkb, a.L, total, per, a.pyr_rows, a.rows[1], a.rows[2], cs, a.scale,
+                     a.H_kv, a.N, a.Npad, a.nqb, a.nkb, a.L, total, per, a.pyr_rows, a.rows[1], a.rows[2], cs, a.scale,
                      a.causal ? 1 : 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -647,8 +669,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows_all = a.N + a.pyr_rows;
   hipLaunchKernelGGL((pyramid_attn_bwd_dkdv_kernel<T, D>), dim3(8 * per2), dim3(256), 0, stream, q,
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.k_pyr),
-                     static_cast<const T*>(a.v_pyr), a.level_map, a.lse, a.Dr, dout, a.dkw, a.dvw, a.H, a.H_kv, a.N,
-                     a.nqb, a.nkb, a.L, a.q_block, items, per2, a.pyr_rows, rows_all, geo, cs, a.scale,
+                     static_cast<const T*>(a.v_pyr), a.level_map, a.lse2, a.Dr, dout, a.dkw, a.dvw, a.H, a.H_kv, a.N,
+                     a.Npad, a.nqb, a.nkb, a.L, a.q_block, items, per2, a.pyr_rows, rows_all, geo, cs, a.scale,
                      a.causal ? 1 : 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

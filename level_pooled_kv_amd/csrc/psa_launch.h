@@ -57,7 +57,9 @@ struct BwdArgs {
   const void* q; const void* k; const void* v; const void* k_pyr; const void* v_pyr;
   const int8_t* level_map; const void* o; const float* lse; const void* dout;
   void* dq; void* dk; void* dv;
-  float* Dr;                     // workspace: [B, H, N] row dots <dO, O>
+  float* lse2;                   // workspace: [B, H, Npad] lse in base 2 (+inf: no key, or padding)
+  float* Dr;                     // workspace: [B, H, Npad] row dots <dO, O> (0 on padding)
+  int Npad;                      // N rounded up to a multiple of 64
   float* dkw; float* dvw;        // workspace: [B, H_kv, N + pyr_rows, d] float32 per-level pooled gradients
   int B, H, H_kv, N, d, q_block, nqb, nkb, L;
   bool bf16;
