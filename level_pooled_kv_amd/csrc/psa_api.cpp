@@ -88,14 +88,16 @@ float effective_scale(const psa_problem_t* p) {
 
 // Mask workspace: mean queries [B, H, nqb, d] then block scores [B, H, nqb, stride],
 // both float32 (the first part's size is a multiple of 256 bytes, so the second
-// stays 16-byte aligned).
+// stays 16-byte aligned), then one byte per score row (rows the exact pass redoes).
 size_t mask_qbar_bytes(const psa_problem_t* p) {
   return (size_t)p->B * p->H * ceil_div(p->N, p->q_block) * p->d * sizeof(float);
 }
-size_t mask_workspace(const psa_problem_t* p) {
+size_t mask_score_bytes(const psa_problem_t* p) {
   const int nkb = (int)ceil_div(p->N, psa::kKvBlock);
-  return mask_qbar_bytes(p) +
-         (size_t)p->B * p->H * ceil_div(p->N, p->q_block) * psa::mask_score_stride(nkb) * sizeof(float);
+  return (size_t)p->B * p->H * ceil_div(p->N, p->q_block) * psa::mask_score_stride(nkb) * sizeof(float);
+}
+size_t mask_workspace(const psa_problem_t* p) {
+  return mask_qbar_bytes(p) + mask_score_bytes(p) + (size_t)p->B * p->H * ceil_div(p->N, p->q_block);
 }
 
 #define REQUIRE_PTR(ptr, name)                                                        \
@@ -221,6 +223,8 @@ static psa_status_t estimate_mask_common(const psa_problem_t* prob, const void* 
   a.q = q; a.k_bar = k_bar; a.level_map = level_map; a.cmass = cmass_out;
   a.qbar = static_cast<float*>(workspace);
   a.z = reinterpret_cast<float*>(static_cast<char*>(workspace) + mask_qbar_bytes(prob));
+  a.need_exact = reinterpret_cast<uint8_t*>(static_cast<char*>(workspace) + mask_qbar_bytes(prob) +
+                                            mask_score_bytes(prob));
   a.B = prob->B; a.H = prob->H; a.H_kv = prob->H_kv; a.N = prob->N; a.d = prob->d;
   a.q_block = prob->q_block;
   a.nqb = (int)ceil_div(prob->N, prob->q_block);

@@ -24,6 +24,7 @@ struct MaskArgs {
   const void* q; const float* k_bar; int8_t* level_map; float* cmass;
   float* qbar;                   // workspace: [B, H, nqb, d] mean queries
   float* z;                      // workspace: [B, H, nqb, mask_score_stride(nkb)] block scores
+  uint8_t* need_exact;           // workspace: [B, H, nqb] rows with equal scores (exact pass)
   int B, H, H_kv, N, d, q_block, nqb, nkb, L, n_dense_prefix;
   bool bf16;
   float scale;

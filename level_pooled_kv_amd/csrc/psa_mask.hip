@@ -162,16 +162,18 @@ block_score_kernel(const float* __restrict__ qbar, const float* __restrict__ kba
   }
 }
 
+// Butterfly reductions over the wave with VALU cross-lane moves; every lane gets the result.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  const int lane = lane_id();
+  x = fmaxf(x, __uint_as_float(xor_lane<1>(__float_as_uint(x), lane)));
+  x = fmaxf(x, __uint_as_float(xor_lane<2>(__float_as_uint(x), lane)));
+  x = fmaxf(x, __uint_as_float(xor_lane<4>(__float_as_uint(x), lane)));
+  x = fmaxf(x, __uint_as_float(xor_lane<8>(__float_as_uint(x), lane)));
+  x = fmaxf(x, __uint_as_float(xor_lane<16>(__float_as_uint(x), lane)));
+  x = fmaxf(x, __uint_as_float(xor_lane<32>(__float_as_uint(x), lane)));
   return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x, lane_id()); }
 
 // Sort key: ascending key order = score descending, then block index ascending.
 // The high word is an order-reversing bijection of the float's bits (so the score
@@ -297,23 +299,30 @@ __device__ __forceinline__ float wave_exclusive_sum(float tot, int lane) {
   return incl - tot;
 }
 
-// One wave per query-block row. Fast path: sort the 32-bit score keys; with no two
-// equal scores the mass ranked ahead of a block is a prefix of the sorted masses, so
-// level l takes exactly the blocks whose key is at most the key at the last sorted
-// position with prefix mass below tau_l. Rows with equal scores (ties are broken by
-// block index) and calls that want the cumulative mass itself take the exact path:
-// a sort of 64-bit (score, index) keys. Both paths sum the same masses in the same
-// order, so they give the same levels.
-template <int E, bool RANKED>
+// One wave per query-block row. Fast path (no cmass): sort the 32-bit score keys; with
+// no two equal scores the mass ranked ahead of a block is a prefix of the sorted masses,
+// so level l takes exactly the blocks whose key is at most the key at the last sorted
+// position with prefix mass below tau_l. Exact path, for rows with equal scores (ties
+// are broken by block index) and for calls that want the cumulative mass itself: sort
+// 64-bit (score, index) keys. Both paths sum the same masses in the same order, so they
+// give the same levels. MODE 0 runs both in one kernel (the exact path only where the
+// fast one finds a tie); for long rows the two are separate kernels, which keeps the
+// fast one small enough for several waves per SIMD: MODE 1 is the fast path, flagging
+// tied rows in need_exact, MODE 2 the exact path over the flagged rows (every row when
+// need_exact is null).
+template <int E, bool RANKED, int MODE>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
-                   int N, int nkb, int nrows, int L, int n_dense_prefix,
+                   uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
                    float tau0, float tau1, float tau2, float tau3, RankFractions frac,
                    int q_block, int nqb, int causal) {
   constexpr int NP = 64 * E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * (kMaskThreads / 64) + wave;
   if (row >= nrows) return;                 // whole wave; no barrier in this kernel
+  if constexpr (MODE == 2) {
+    if (need_exact != nullptr && need_exact[row] == 0) return;
+  }
   // Causal use: the row ranks only the nvis blocks that hold a token at or before its
   // query block's last row; blocks from dfirst on reach the block's own rows and stay at
   // full resolution (a pooled key would mix in later tokens); later blocks are pruned.
@@ -369,7 +378,7 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     }
   }
 
-  if (cmass == nullptr) {
+  if (MODE == 1 || (MODE == 0 && cmass == nullptr)) {
     uint32_t orig[E], key[E];
 #pragma unroll
     for (int r = 0; r < E; ++r) {
@@ -382,7 +391,9 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     for (int r = 0; r + 1 < E; ++r) tie |= key[r] == key[r + 1] && key[r] != kPadKey32;
     const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
     tie |= lane < 63 && key[E - 1] == next_first && key[E - 1] != kPadKey32;
-    if (__ballot(tie) == 0) {
+    const bool any_tie = __ballot(tie) != 0;
+    if (MODE == 1 && lane == 0) need_exact[row] = any_tie ? 1 : 0;
+    if (!any_tie) {
       // cnt[l]: how many blocks, in rank order, take level l or a finer one
       int cnt[kMaxLevels] = {0, 0, 0, 0};
       if constexpr (RANKED) {
@@ -396,14 +407,17 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
           tot += p[r];
         }
         float run = wave_exclusive_sum(tot, lane);
+        int lc[kMaxLevels] = {0, 0, 0, 0};   // this lane's blocks with C below each threshold
 #pragma unroll
         for (int r = 0; r < E; ++r) {
           const float C = run;
           run += p[r];
           const bool real = key[r] != kPadKey32;
 #pragma unroll
-          for (int l = 0; l < kMaxLevels; ++l) cnt[l] += (int)__popcll(__ballot(real && C < tau[l]));
+          for (int l = 0; l < kMaxLevels; ++l) lc[l] += real && C < tau[l] ? 1 : 0;
         }
+#pragma unroll
+        for (int l = 0; l < kMaxLevels; ++l) cnt[l] = (int)wave_sum((float)lc[l]);   // exact: counts < 2^24
       }
       // key at sorted position cnt[l] - 1: the last block level l (or a lower one) takes
       uint32_t cut[kMaxLevels];
@@ -430,6 +444,7 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
       }
       return;
     }
+    if constexpr (MODE == 1) return;
   }
 
   // ---- exact path: sort (score, index) keys
@@ -478,9 +493,22 @@ template <int E, bool RANKED>
 static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
   RankFractions frac;
   for (int l = 0; l < kMaxLevels; ++l) frac.f[l] = a.frac[l];
-  hipLaunchKernelGGL((block_level_kernel<E, RANKED>), dim3((nrows + 3) / 4), dim3(kMaskThreads), 0, stream,
-                     a.z, a.level_map, a.cmass, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0], a.tau[1],
-                     a.tau[2], a.tau[3], frac, a.q_block, a.nqb, a.causal ? 1 : 0);
+  const dim3 grid((nrows + 3) / 4);
+  const int causal = a.causal ? 1 : 0;
+  if constexpr (E <= 8) {
+    hipLaunchKernelGGL((block_level_kernel<E, RANKED, 0>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
+                       a.cmass, nullptr, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0], a.tau[1], a.tau[2],
+                       a.tau[3], frac, a.q_block, a.nqb, causal);
+  } else {
+    // without cmass: the fast pass, then the exact pass over the rows it flagged
+    if (a.cmass == nullptr)
+      hipLaunchKernelGGL((block_level_kernel<E, RANKED, 1>), grid, dim3(kMaskThreads), 0, stream, a.z,
+                         a.level_map, a.cmass, a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0],
+                         a.tau[1], a.tau[2], a.tau[3], frac, a.q_block, a.nqb, causal);
+    hipLaunchKernelGGL((block_level_kernel<E, RANKED, 2>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
+                       a.cmass, a.cmass == nullptr ? a.need_exact : nullptr, a.N, a.nkb, nrows, a.L,
+                       a.n_dense_prefix, a.tau[0], a.tau[1], a.tau[2], a.tau[3], frac, a.q_block, a.nqb, causal);
+  }
 }
 
 template <int E>

@@ -42,12 +42,18 @@ def test_sizes(psa):
     p = prob(psa)
     assert p.pyramid_rows == sum(math.ceil(32760 / 2 ** l) for l in (1, 2, 3))
     # mean queries [B,H,nqb,d] + block scores [B,H,nqb,512] (512 KV blocks, already a power of two)
-    assert p.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK) == 1 * 12 * 256 * 128 * 4 + 1 * 12 * 256 * 512 * 4
+    # + one flag byte per score row
+    assert p.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK) == 12 * 256 * 128 * 4 + 12 * 256 * 512 * 4 + 12 * 256
     # score rows are padded to a power of two >= 64: 278 KV blocks -> 512, 32 -> 64
     assert (prob(psa, H=48, H_kv=48, N=17776, d=64).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
-            == 48 * 139 * 64 * 4 + 48 * 139 * 512 * 4)
+            == 48 * 139 * 64 * 4 + 48 * 139 * 512 * 4 + 48 * 139)
     assert (prob(psa, H=2, H_kv=2, N=2048, d=64, q_block=64).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
-            == 2 * 32 * 64 * 4 + 2 * 32 * 64 * 4)
+            == 2 * 32 * 64 * 4 + 2 * 32 * 64 * 4 + 2 * 32)
+    # backward: lse (base 2) and row dots [B,H,Npad] (N padded to 64 rows), each on a 256-byte
+    # boundary, then float32 per-level gradients of K and V [B,H_kv,N+pyramid rows,d]
+    r256 = lambda x: (x + 255) // 256 * 256
+    rows_all = 32760 + p.pyramid_rows
+    assert p.workspace_bytes(psa.PSA_WS_ATTENTION_BWD) == 2 * r256(12 * 32768 * 4) + 2 * r256(12 * rows_all * 128 * 4)
     assert p.workspace_bytes(psa.PSA_WS_ATTENTION_FWD) == 0
     assert prob(psa, num_levels=1).pyramid_rows == 0
     assert prob(psa, N=2045, num_levels=2).pyramid_rows == 1023
