@@ -299,17 +299,17 @@ __device__ __forceinline__ float wave_exclusive_sum(float tot, int lane) {
   return incl - tot;
 }
 
-// One wave per query-block row. Fast path (no cmass): sort the 32-bit score keys; with
-// no two equal scores the mass ranked ahead of a block is a prefix of the sorted masses,
-// so level l takes exactly the blocks whose key is at most the key at the last sorted
-// position with prefix mass below tau_l. Exact path, for rows with equal scores (ties
-// are broken by block index) and for calls that want the cumulative mass itself: sort
-// 64-bit (score, index) keys. Both paths sum the same masses in the same order, so they
-// give the same levels. MODE 0 runs both in one kernel (the exact path only where the
-// fast one finds a tie); for long rows the two are separate kernels, which keeps the
-// fast one small enough for several waves per SIMD: MODE 1 is the fast path, flagging
-// tied rows in need_exact, MODE 2 the exact path over the flagged rows (every row when
-// need_exact is null).
+// One wave per query-block row. Fast path (no cmass): sort the 32-bit score keys; the
+// mass ranked ahead of a block is a prefix of the sorted masses, so level l takes the
+// blocks whose key is at most the key at the last sorted position with prefix mass
+// below tau_l, unless that key continues past the cut (equal scores, which the rule
+// orders by block index). Exact path, for such rows and for calls that want the
+// cumulative mass itself: sort 64-bit (score, index) keys. Both paths sum the same
+// masses in the same order, so they give the same levels. MODE 0 runs both in one
+// kernel (the exact path only for rows the fast one cannot settle); for long rows the
+// two are separate kernels, which keeps the fast one small enough for several waves
+// per SIMD: MODE 1 is the fast path, flagging such rows in need_exact, MODE 2 the exact
+// path over the flagged rows (every row when need_exact is null).
 template <int E, bool RANKED, int MODE>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
@@ -386,50 +386,58 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
       key[r] = orig[r];
     }
     wave_bitonic_sort32<E>(key, lane);
-    bool tie = false;
+    // cnt[l]: how many blocks, in rank order, take level l or a finer one. Blocks with
+    // equal scores have equal masses, so the prefix sums along the sorted keys do not
+    // depend on how the sort ordered them among themselves.
+    int cnt[kMaxLevels] = {0, 0, 0, 0};
+    if constexpr (RANKED) {
 #pragma unroll
-    for (int r = 0; r + 1 < E; ++r) tie |= key[r] == key[r + 1] && key[r] != kPadKey32;
-    const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
-    tie |= lane < 63 && key[E - 1] == next_first && key[E - 1] != kPadKey32;
-    const bool any_tie = __ballot(tie) != 0;
-    if (MODE == 1 && lane == 0) need_exact[row] = any_tie ? 1 : 0;
-    if (!any_tie) {
-      // cnt[l]: how many blocks, in rank order, take level l or a finer one
-      int cnt[kMaxLevels] = {0, 0, 0, 0};
-      if constexpr (RANKED) {
+      for (int l = 0; l < kMaxLevels; ++l) cnt[l] = K[l];
+    } else {
+      float p[E], tot = 0.f;
 #pragma unroll
-        for (int l = 0; l < kMaxLevels; ++l) cnt[l] = K[l];
-      } else {
-        float p[E], tot = 0.f;
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          p[r] = key[r] != kPadKey32 ? __expf(key32_score(key[r]) - mx) * inv_s : 0.f;
-          tot += p[r];
-        }
-        float run = wave_exclusive_sum(tot, lane);
-        int lc[kMaxLevels] = {0, 0, 0, 0};   // this lane's blocks with C below each threshold
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const float C = run;
-          run += p[r];
-          const bool real = key[r] != kPadKey32;
-#pragma unroll
-          for (int l = 0; l < kMaxLevels; ++l) lc[l] += real && C < tau[l] ? 1 : 0;
-        }
-#pragma unroll
-        for (int l = 0; l < kMaxLevels; ++l) cnt[l] = (int)wave_sum((float)lc[l]);   // exact: counts < 2^24
+      for (int r = 0; r < E; ++r) {
+        p[r] = key[r] != kPadKey32 ? __expf(key32_score(key[r]) - mx) * inv_s : 0.f;
+        tot += p[r];
       }
-      // key at sorted position cnt[l] - 1: the last block level l (or a lower one) takes
-      uint32_t cut[kMaxLevels];
+      float run = wave_exclusive_sum(tot, lane);
+      int lc[kMaxLevels] = {0, 0, 0, 0};   // this lane's blocks with C below each threshold
 #pragma unroll
-      for (int l = 0; l < kMaxLevels; ++l) {
-        const int pos = cnt[l] - 1;
-        uint32_t v = key[0];
+      for (int r = 0; r < E; ++r) {
+        const float C = run;
+        run += p[r];
+        const bool real = key[r] != kPadKey32;
 #pragma unroll
-        for (int r = 1; r < E; ++r)
-          if (pos >= 0 && pos % E == r) v = key[r];
-        cut[l] = pos >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v, pos / E) : 0u;
+        for (int l = 0; l < kMaxLevels; ++l) lc[l] += real && C < tau[l] ? 1 : 0;
       }
+#pragma unroll
+      for (int l = 0; l < kMaxLevels; ++l) cnt[l] = (int)wave_sum((float)lc[l]);   // exact: counts < 2^24
+    }
+    // cut[l]: key at sorted position cnt[l] - 1, the last block level l (or a finer one)
+    // takes. Equal scores matter only where more than cnt[l] keys are <= cut[l], i.e. a
+    // key after the cut equals it: then the index order decides which of them are in,
+    // and the row takes the exact path.
+    uint32_t cut[kMaxLevels];
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) {
+      const int pos = cnt[l] - 1;
+      uint32_t v = key[0];
+#pragma unroll
+      for (int r = 1; r < E; ++r)
+        if (pos >= 0 && pos % E == r) v = key[r];
+      cut[l] = pos >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v, pos / E) : 0u;
+    }
+    int le[kMaxLevels] = {0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < E; ++r)
+#pragma unroll
+      for (int l = 0; l < kMaxLevels; ++l) le[l] += orig[r] <= cut[l] ? 1 : 0;
+    bool split = false;
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l)
+      if (l < L && cnt[l] > 0) split |= (int)wave_sum((float)le[l]) > cnt[l];   // exact: counts < 2^24
+    if (MODE == 1 && lane == 0) need_exact[row] = split ? 1 : 0;
+    if (!split) {
 #pragma unroll
       for (int r = 0; r < E; ++r) {
         const int j = E * lane + r;

@@ -190,6 +190,35 @@ def test_mask_equal_scores(psa):
     check_mask(lev.cpu().numpy(), ora["mask"], tau, 4, 0, label="equal scores")
 
 
+@pytest.mark.parametrize("N", [40000, 70000], ids=["625 blocks", "1094 blocks"])
+def test_mask_equal_scores_long_rows(psa, N):
+    # Rows of more than 512 KV blocks run as a fast kernel and an exact kernel over the
+    # rows it flags. 300 identical KV blocks give every row a group of equal scores, and
+    # the thresholds split that group in some rows: there the index order decides.
+    d, L = 64, 4
+    q, k, v = random_qkv(N // 1000, 1, 1, 1, N, d, "bf16")
+    k[:, :, 64:64 * 301] = np.tile(k[:, :, 64:128], (1, 1, 300, 1))
+    tau = (0.02, 0.1, 0.3, 0.6)
+    ora = o.estimate_mask(q, k, 128, 64, tau, L, 1 / math.sqrt(d))
+    C = ora["cmass"][..., 1:301]
+    split_rows = sum(bool(np.any((C < t).any(-1) & (C >= t).any(-1))) for t in tau)
+    assert split_rows > 0, "no threshold falls inside the group of equal scores"
+    prob = psa.Problem(B=1, H=1, H_kv=1, N=N, d=d, q_block=128, num_levels=L, dtype="bf16")
+    say(f"mask with 300 equal-score blocks, N={N} ({prob.nkb} blocks per row)")
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    _, _, kbar = psa.psa_build_pyramid(prob, kd, to_device(v, "bf16"))
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, tau)
+    lev_c, _ = psa.psa_estimate_mask(prob, qd, kbar, tau, want_cmass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lev, lev_c)
+    lev_g = lev.cpu().numpy()
+    check_mask(lev_g, ora, tau, L, 0, label=f"equal scores, N={N}")
+    # within the group the levels never get finer as the block index grows
+    grp = lev_g[..., 1:301].astype(int)
+    grp[grp < 0] = 9
+    assert np.all(np.diff(grp, axis=-1) >= 0)
+
+
 def test_deterministic(psa):
     q, k, v = random_qkv(9, 1, 2, 2, 3000, 128, "bf16")
     prob = psa.Problem(B=1, H=2, H_kv=2, N=3000, d=128, q_block=128, num_levels=4, dtype="bf16")

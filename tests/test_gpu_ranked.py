@@ -96,6 +96,19 @@ def test_ranked_equal_scores(psa):
     assert np.all(np.diff(grp, axis=-1) >= 0)
 
 
+def test_ranked_equal_scores_long_rows(psa):
+    # 1094 blocks per row (fast kernel plus exact kernel over flagged rows); 300 equal
+    # scores in every row, which the rank cuts split
+    N = 70000
+    q, k, v = random_qkv(21, 1, 1, 1, N, 64, "bf16")
+    k[:, :, 64:64 * 301] = np.tile(k[:, :, 64:128], (1, 1, 300, 1))
+    ora, lev = run_ranked(psa, "ranked, 300 equal scores, 1094 blocks", q, k, v, H=1, H_kv=1, d=64, q_block=128,
+                          L=4, dtype="bf16", fractions=(0.05, 0.15, 0.3, 0.5), attention=False)
+    grp = lev[..., 1:301].astype(int)
+    grp[grp < 0] = 9
+    assert np.all(np.diff(grp, axis=-1) >= 0)
+
+
 def test_ranked_all_blocks_level0_equals_threshold_one(psa):
     q, k, v = random_qkv(12, 1, 2, 2, 1500, 128, "bf16")
     prob = psa.Problem(B=1, H=2, H_kv=2, N=1500, d=128, q_block=128, num_levels=4, dtype="bf16")
