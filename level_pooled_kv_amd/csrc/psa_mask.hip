@@ -386,6 +386,13 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
       key[r] = orig[r];
     }
     wave_bitonic_sort32<E>(key, lane);
+    // equal scores anywhere in the row (neighbours in sorted order)?
+    bool tie = false;
+#pragma unroll
+    for (int r = 0; r + 1 < E; ++r) tie |= key[r] == key[r + 1] && key[r] != kPadKey32;
+    const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
+    tie |= lane < 63 && key[E - 1] == next_first && key[E - 1] != kPadKey32;
+    const bool any_tie = __ballot(tie) != 0;
     // cnt[l]: how many blocks, in rank order, take level l or a finer one. Blocks with
     // equal scores have equal masses, so the prefix sums along the sorted keys do not
     // depend on how the sort ordered them among themselves.
@@ -427,15 +434,17 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
         if (pos >= 0 && pos % E == r) v = key[r];
       cut[l] = pos >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v, pos / E) : 0u;
     }
-    int le[kMaxLevels] = {0, 0, 0, 0};
-#pragma unroll
-    for (int r = 0; r < E; ++r)
-#pragma unroll
-      for (int l = 0; l < kMaxLevels; ++l) le[l] += orig[r] <= cut[l] ? 1 : 0;
     bool split = false;
+    if (any_tie) {
+      int le[kMaxLevels] = {0, 0, 0, 0};
 #pragma unroll
-    for (int l = 0; l < kMaxLevels; ++l)
-      if (l < L && cnt[l] > 0) split |= (int)wave_sum((float)le[l]) > cnt[l];   // exact: counts < 2^24
+      for (int r = 0; r < E; ++r)
+#pragma unroll
+        for (int l = 0; l < kMaxLevels; ++l) le[l] += orig[r] <= cut[l] ? 1 : 0;
+#pragma unroll
+      for (int l = 0; l < kMaxLevels; ++l)
+        if (l < L && cnt[l] > 0) split |= (int)wave_sum((float)le[l]) > cnt[l];   // exact: counts < 2^24
+    }
     if (MODE == 1 && lane == 0) need_exact[row] = split ? 1 : 0;
     if (!split) {
 #pragma unroll
