@@ -149,7 +149,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
     }
   };
   // Both K and V are read row-wise (A operands) and K also transposed; both tiles use
-  // the K swizzle.
+  // the swizzle of tiles read both ways (qt_swz).
   auto issue_tile = [&](int t, auto P) {
     constexpr int buf = P();
     const TileInfo ti = tile_info(t);
@@ -170,7 +170,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
       const int prow = blk * seglen + (row & (seglen - 1));
       const bool ok = vseg && prow < rows_lv;
       const int rowel = (ok ? prow : 0) * D;
-      const uint32_t off = (uint32_t)((rowel + 8 * (st_pchunk ^ k_swz<D>(row))) * (int)sizeof(T));
+      const uint32_t off = (uint32_t)((rowel + 8 * (st_pchunk ^ qt_swz<D>(row))) * (int)sizeof(T));
       if constexpr (kDirect) {
         const int blkoff = (wave * BPW + i) * 512;
         __builtin_amdgcn_global_load_lds((gbl_void*)(kb + off), (lds_void*)(kbuf(P) + blkoff), 16, 0, 0);
@@ -232,7 +232,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
       const int krow = 32 * kb + l32 + zero;
       const uint16_t* kr = Kb + krow * D;
       const uint16_t* vr = Vb + krow * D;
-      const int swz = k_swz<D>(krow);
+      const int swz = qt_swz<D>(krow);
 #pragma unroll
       for (int c = 0; c < C::kQc; ++c) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * c + half) ^ swz) * 8));
@@ -273,7 +273,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
           for (int j = 0; j < 2; ++j) {
             const int row = 16 * c + 8 * j + tr_row + zero;
             const int col = 32 * tt + tr_col;
-            const int chunk = (col >> 3) ^ k_swz<D>(row);
+            const int chunk = (col >> 3) ^ qt_swz<D>(row);
             part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Kb + row * D + chunk * 8 + (col & 7)));
           }
           const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -363,7 +363,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
   const int prow0 = kt * 64;
   const int j0 = kt << lvl;                   // first KV block of the tile
 
-  // ---- stage the tile's pooled K and V rows (bf16, K swizzle), per-key constants
+  // ---- stage the tile's pooled K and V rows (bf16, qt_swz swizzle), per-key constants
   {
     const T* ksrc = lvl == 0 ? k + (int64_t)bg * N * D : kp + ((int64_t)bg * pyr_rows + geo.poff[lvl]) * D;
     const T* vsrc = lvl == 0 ? v + (int64_t)bg * N * D : vp + ((int64_t)bg * pyr_rows + geo.poff[lvl]) * D;
@@ -383,7 +383,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
           vv = rv.bf16();
         }
       }
-      const int pc = ch ^ k_swz<D>(row);
+      const int pc = ch ^ qt_swz<D>(row);
       st128(Ks + row * D + pc * 8, kk);
       st128(Vs + row * D + pc * 8, vv);
     }
@@ -436,7 +436,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
       const int ktok = s_ltok[krow];
       for (int r0 = i * q_block; r0 < min((i + 1) * q_block, N); r0 += 64) {
         __syncthreads();                      // the previous chunk's reads are done
-        // stage Q and dO rows r0..r0+63 (K swizzle; rows past N read row N-1 and are
+        // stage Q and dO rows r0..r0+63 (qt_swz swizzle; rows past N read row N-1 and are
         // never used: their lse2 is +inf, so P = dS = 0). bf16: direct global -> LDS
         // loads, each wave filling 1 KB blocks of RPK rows; all loads issued before any wait.
         {
@@ -450,7 +450,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
               const int blk = wave * BPWV + bb;
               const int row = blk * RPK + lrow;
               const int64_t r = min(r0 + row, N - 1);
-              const int lc = lch ^ k_swz<D>(row);     // logical chunk stored in physical slot lch
+              const int lc = lch ^ qt_swz<D>(row);     // logical chunk stored in physical slot lch
               __builtin_amdgcn_global_load_lds((gbl_void*)(q + (bh * N + r) * D + lc * 8), (lds_void*)(Qs + blk * 512),
                                                16, 0, 0);
               __builtin_amdgcn_global_load_lds((gbl_void*)(dout + (bh * N + r) * D + lc * 8),
@@ -467,7 +467,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
             for (int bb = 0; bb < BPWV; ++bb) {
               const int row = (wave * BPWV + bb) * RPK + lrow;
               const int64_t r = min(r0 + row, N - 1);
-              const int lc = lch ^ k_swz<D>(row);
+              const int lc = lch ^ qt_swz<D>(row);
               rq[bb].load(reinterpret_cast<const float*>(q) + (bh * N + r) * D + lc * 8);
               rd[bb].load(reinterpret_cast<const float*>(dout) + (bh * N + r) * D + lc * 8);
             }
@@ -494,7 +494,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
 #pragma unroll
         for (int x = 0; x < 16; ++x) sacc[x] = dpacc[x] = 0.f;
         const int qrow = 32 * qh + l32;
-        const int qswz = k_swz<D>(qrow), kswz = k_swz<D>(krow);
+        const int qswz = qt_swz<D>(qrow), kswz = qt_swz<D>(krow);
 #pragma unroll
         for (int c = 0; c < kQc; ++c) {
           const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + qrow * D + (((2 * c + half) ^ qswz) * 8));
@@ -533,7 +533,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
             for (int j = 0; j < 2; ++j) {
               const int row = 32 * qh + 16 * cc + 8 * j + tr_row;
               const int col = 32 * tt + tr_col;
-              const int chunk = (col >> 3) ^ k_swz<D>(row);
+              const int chunk = (col >> 3) ^ qt_swz<D>(row);
               pd[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Os + row * D + chunk * 8 + (col & 7)));
               pq[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Qs + row * D + chunk * 8 + (col & 7)));
             }

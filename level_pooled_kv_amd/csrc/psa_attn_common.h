@@ -45,6 +45,13 @@ template <int D> __device__ __forceinline__ int k_swz(int row) {
 template <int D> __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
+// Tiles read both ways (16-byte operand rows and transposing reads: the backward's Q,
+// dO and K tiles). For D = 128 the two 2-bit fields of row & 15 are swapped: still a
+// permutation over 16 consecutive rows, and the 4 rows x 2 chunks that one 16-lane
+// group of a transposing read touches land on 8 distinct chunks.
+template <int D> __device__ __forceinline__ int qt_swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : k_swz<D>(row);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
