@@ -16,10 +16,13 @@
 //    matrix cores (v_mfma_f32_32x32x2_f32), one 32 x 32 tile per wave, into a
 //    workspace row of n_pad floats per query block.
 //  * block_level_kernel: one wave per query-block row: softmax of the row, a
-//    bitonic sort of (score, index) keys held in registers (n_pad / 64 per lane;
-//    partners in other lanes come through cross-lane shuffles, so no LDS and no
-//    workgroup barrier), a wave-wide exclusive scan of the masses in rank order,
-//    the threshold compares and the int8 level writes.
+//    bitonic sort of score keys held in registers (n_pad / 64 per lane; partners
+//    in other lanes come through cross-lane shuffles, so no LDS and no workgroup
+//    barrier), a wave-wide exclusive scan of the masses in rank order, the
+//    threshold compares and the int8 level writes. 32-bit keys settle a row unless
+//    a cut splits a group of equal scores; such rows, and calls that want the
+//    cumulative mass, sort 64-bit (score, index) keys (for rows of more than 512
+//    blocks in a second kernel over the rows the first one flags).
 //    Its ranked form (the quantile rule the top168.com ablation compares with
 //    thresholds; fixed shares of the score-ranked blocks per level: skillmd.com,
 //    "Level assignment") gives the block at rank r the lowest level l with
