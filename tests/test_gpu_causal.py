@@ -159,6 +159,44 @@ def test_causal_dense_map_equals_causal_attention(psa):
     check_attention(to_host(out), Od, "causal dense")
 
 
+@pytest.mark.parametrize("ranked", [False, True], ids=["thresholds", "ranked"])
+def test_causal_mask_long_rows(psa, ranked):
+    # 625 KV blocks per row: the fast and exact level kernels (separate for rows this
+    # long) under causal use, with 300 equal-score blocks so that some cuts split a tie
+    N, d, L = 40000, 64, 4
+    q, k, v = random_qkv(33, 1, 1, 1, N, d, "bf16")
+    k[:, :, 64:64 * 301] = np.tile(k[:, :, 64:128], (1, 1, 300, 1))
+    s = 1.0 / math.sqrt(d)
+    prob = psa.Problem(B=1, H=1, H_kv=1, N=N, d=d, q_block=128, num_levels=L, dtype="bf16", causal=True)
+    tau, fr = (0.02, 0.1, 0.3, 0.6), (0.05, 0.15, 0.3, 0.5)
+    say(f"causal mask, {prob.nkb} blocks per row, {'ranked' if ranked else 'thresholds'}")
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    _, _, kbar = psa.psa_build_pyramid(prob, kd, to_device(v, "bf16"))
+    if ranked:
+        lev, _ = psa.psa_estimate_mask_ranked(prob, qd, kbar, fr)
+        lev_c, _ = psa.psa_estimate_mask_ranked(prob, qd, kbar, fr, want_cmass=True)
+    else:
+        lev, _ = psa.psa_estimate_mask(prob, qd, kbar, tau)
+        lev_c, _ = psa.psa_estimate_mask(prob, qd, kbar, tau, want_cmass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lev, lev_c)
+    lev_g = lev.cpu().numpy()
+    vis, diag = o.causal_blocks(N, 128, 64)
+    assert np.all(lev_g[..., ~vis] == -1) and np.all(lev_g[..., diag] == 0)
+    if ranked:
+        m = o.estimate_mask_ranked(q, k, 128, 64, fr, L, s, causal=True)
+        nvis = vis.sum(axis=-1)
+        for i in range(0, lev_g.shape[2], 7):
+            nv = int(nvis[i])
+            sub = {"z": m["z"][:, :, i:i + 1, :nv], "levels": m["levels"][:, :, i:i + 1, :nv]}
+            check_mask_ranked(lev_g[:, :, i:i + 1, :nv], sub, o.rank_counts(fr, L, nv), L, 0,
+                              label=f"causal ranked row {i}", check_counts=False)
+    else:
+        m = o.estimate_mask(q, k, 128, 64, tau, L, s, causal=True)
+        check_mask(lev_g, m, tau, L, 0, label="causal, long rows")
+    say("causal mask, long rows: ok")
+
+
 def test_causal_full_workload(psa):
     w = get_workload("wan13b_causal")
     L, s = w.num_levels, w.scale
