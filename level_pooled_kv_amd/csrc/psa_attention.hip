@@ -351,9 +351,9 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 
     // O^T += V^T P^T; the A operand is fetched transposed from row-major V
 #pragma unroll
-    for (int tt = 0; tt < C::kDt; ++tt) {
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int tt = 0; tt < C::kDt; ++tt) {
         bf16x4 part[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -366,7 +366,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, preg[c], oacc[tt], 0, 0, 0);
         if constexpr (kDirect) {
-          const int j = tt * 4 + c;
+          const int j = c * C::kDt + tt;
           if ((j + 1) % SV == 0) dma_v(st, j / SV, PN{});
         }
       }
