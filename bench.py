@@ -47,7 +47,7 @@ def attention_source_hash() -> str:
 
 def attention_kernel_name(d: int, q_block: int, dtype: str) -> str:
     t = "bf16" if dtype == "bf16" else "float"
-    return f"pyramid_attn_fwd_kernel<{t},{d},{q_block // 32}>"
+    return f"pyramid_attn_fwd_kernel<{t},{d},4,{128 // q_block}>"
 
 
 def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, d: int,

@@ -10,7 +10,10 @@
 //
 // How (decoupled logical blocks / hardware tiles, chatpaper.ai abstract and the
 // top168.com kernel paragraph, re-designed for CDNA4):
-//  * One workgroup per (batch, head, query block); NW waves of 32 query rows each.
+//  * One workgroup per (batch, head, query block) of four waves: 32 query rows each
+//    for 128-row query blocks; for 64-row blocks two row groups x two key halves,
+//    each wave with its own online softmax over its half of every tile, merged at
+//    the end (four waves per workgroup keep two waves per SIMD).
 //    Workgroup ids are remapped so that the eight XCDs each take a contiguous run
 //    of query blocks of the same heads (dispatch is round-robin over XCDs), which
 //    keeps the K/V rows those blocks share in one XCD's L2. Under causal use the
@@ -42,7 +45,12 @@
 
 namespace psa {
 
-template <typename T, int D, int NW>
+// KS = 1: NW waves of 32 query rows each over whole tiles. KS = 2 (64-row query blocks):
+// the NW = 4 waves are 2 row groups x 2 key halves; each wave runs its own online
+// softmax over its 32 keys of every tile, and the two halves' (max, sum, O) states are
+// merged through LDS at the end. This keeps four waves per workgroup, hence two per
+// SIMD, where two-wave workgroups would leave one (the LDS holds two per CU).
+template <typename T, int D, int NW, int KS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                         const T* __restrict__ kp, const T* __restrict__ vp,
@@ -50,6 +58,8 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
                         int H, int H_kv, int N, int nqb, int nkb, int L, int total_items, int per_xcd,
                         int64_t pyr_rows, int rows1, int rows2, float cs /* scale * log2(e) */, int causal) {
   using C = AttnCfg<D, NW>;
+  constexpr int RW = NW / KS;                    // waves per 32-key group: row groups of 32 queries
+  constexpr int KB = 2 / KS;                     // 32-key halves of a tile each wave computes
   constexpr int CPR = C::kCpr, RPB = C::kRpb, BPW = C::kBpw;
   constexpr bool kDirect = sizeof(T) == 2;     // bf16: global -> LDS without registers
   // One LDS object per tile buffer: the wait-count analysis can then tell the direct
@@ -92,12 +102,13 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 
   // ---- compact the level-map row into level-major block lists (wave 0)
   const int8_t* lrow = level_map + (int64_t)item * nkb;   // item == (b*H + h)*nqb + qi
-  const int q0 = qi * (32 * NW);
+  const int q0 = qi * (32 * RW);
   if (wave == 0) build_tile_lists(lrow, nkb, L, N, causal ? q0 / 64 : nkb, blist, tdesc, s_tile);
 
   // ---- Q operand in registers: lane (row = lane%32, half = lane/32) holds d = 16c + 8*half + 0..7
   const int half = lane >> 5, l32 = lane & 31;
-  const int my_row = q0 + 32 * wave + l32;
+  const int khalf = KS == 1 ? 0 : wave / RW;        // key half of every tile
+  const int my_row = q0 + 32 * (KS == 1 ? wave : wave % RW) + l32;
   bf16x8 qreg[C::kQc];
   {
     const T* qrow = q + ((int64_t)bh * N + min(my_row, N - 1)) * D;
@@ -270,20 +281,20 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     Stage st{};
     if constexpr (kDirect) st = stage_addr(min(t + 1, T_total - 1), PN{});
     else if (t + 1 < T_total) issue_tile(t + 1, PN{});
-    constexpr int SK = 2 * C::kQc / BPW, SV = 4 * C::kDt / BPW;   // MFMAs per interleaved load
+    constexpr int SK = KB * C::kQc / BPW, SV = 2 * KB * C::kDt / BPW;   // MFMAs per interleaved load
     const TileInfo ti = tile_info(t);
     const int lvl = ti.lvl;
     const bool irr = ti.irr;
     const uint16_t* Kb = kbuf(P);
     const uint16_t* Vb = vbuf(P);
 
-    // S^T = K Q^T: two 32-key halves
-    f32x16 sacc[2];
+    // S^T = K Q^T: the wave's 32-key halves (kb + KB khalf of the tile)
+    f32x16 sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int x = 0; x < 16; ++x) sacc[kb][x] = 0.f;
-      const int krow = 32 * kb + l32;
+      const int krow = 32 * (kb + KB * khalf) + l32;
       const uint16_t* kr_l = Kb + krow * D;
       const int swz = k_swz<D>(krow);
 #pragma unroll
@@ -298,23 +309,23 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     }
     if (irr) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; ++x)
-          sacc[kb][x] += corr[buf][32 * kb + 8 * (x >> 2) + 4 * half + (x & 3)];
+          sacc[kb][x] += corr[buf][32 * (kb + KB * khalf) + 8 * (x >> 2) + 4 * half + (x & 3)];
     }
     if (ti.diag) {   // causal: a key is seen only by rows at or after its last token
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int x = 0; x < 16; ++x)
-          if (ltok[buf][32 * kb + 8 * (x >> 2) + 4 * half + (x & 3)] > my_row) sacc[kb][x] = -INFINITY;
+          if (ltok[buf][32 * (kb + KB * khalf) + 8 * (x >> 2) + 4 * half + (x & 3)] > my_row) sacc[kb][x] = -INFINITY;
     }
 
     // online softmax (base 2); this tile's keys all carry bias lvl
     float tmax = sacc[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sacc[kb][x]);
     {   // lanes l and l^32 hold the two key halves of one query
@@ -334,12 +345,13 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         for (int x = 0; x < 16; ++x) oacc[tt][x] *= alpha;
       m_run = upd ? mt : m_run;
     }
-    // a row that has seen no key yet (possible only after causal masking) keeps p = 0
-    const float moff = ti.diag && m_run == -INFINITY ? 0.f : lvlf - m_run;
-    bf16x8 preg[4];
+    // a row that has seen no key yet keeps p = 0 (its logits here are all -inf: causal
+    // masking, or with split keys a half tile of only padding rows)
+    const float moff = (KS == 2 || ti.diag) && m_run == -INFINITY ? 0.f : lvlf - m_run;
+    bf16x8 preg[2 * KB];
     float lsum = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2 * KB; ++c) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e], cs, moff));
@@ -351,13 +363,13 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
 
     // O^T += V^T P^T; the A operand is fetched transposed from row-major V
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2 * KB; ++c) {
 #pragma unroll
       for (int tt = 0; tt < C::kDt; ++tt) {
         bf16x4 part[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int row = 16 * c + 8 * j + tr_row;
+          const int row = 16 * (c + 2 * KB * khalf) + 8 * j + tr_row;
           const int col = 32 * tt + tr_col;
           const int chunk = (col >> 3) ^ v_swz<D>(row);
           part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -381,11 +393,41 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     if (t + 1 < T_total) body(t + 1, P1{});
   }
 
+  if constexpr (KS == 2) {
+    // merge the two key halves' softmax states of each query: the khalf = 1 waves hand
+    // (max, partial sums, O^T) to the khalf = 0 waves of the same rows through LDS (the
+    // tile buffers are idle: the loop's last barrier follows its last loads)
+    const int rw = wave % RW;
+    float* xo = reinterpret_cast<float*>(rw == 0 ? K0 : K1);   // [tt][x][lane]
+    float* xs = reinterpret_cast<float*>(V0) + rw * 128;        // [m, l][lane]
+    if (khalf == 1) {
+#pragma unroll
+      for (int tt = 0; tt < C::kDt; ++tt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) xo[(tt * 16 + x) * 64 + lane] = oacc[tt][x];
+      xs[lane] = m_run;
+      xs[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (khalf == 0) {
+      const float m1 = xs[lane], l1 = xs[64 + lane];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+      const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+      for (int tt = 0; tt < C::kDt; ++tt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) oacc[tt][x] = oacc[tt][x] * a0 + xo[(tt * 16 + x) * 64 + lane] * a1;
+      m_run = m;
+    }
+  }
+
   // ---- normalise and write O (and LSE)
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (my_row < N) {
+  if (my_row < N && khalf == 0) {
     T* orow = o + ((int64_t)bh * N + my_row) * D;
 #pragma unroll
     for (int tt = 0; tt < C::kDt; ++tt) {
@@ -406,13 +448,13 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int KS>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   const int total = a.B * a.H * a.nqb;
   // slots per XCD; causal with an even nqb hands out whole (i, nqb-1-i) pairs
   const int per = a.causal && a.nqb % 2 == 0 ? 2 * ((total / 2 + 7) / 8) : (total + 7) / 8;
   const float cs = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((pyramid_attn_fwd_kernel<T, D, NW>), dim3(8 * per), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((pyramid_attn_fwd_kernel<T, D, NW, KS>), dim3(8 * per), dim3(NW * 64), 0, stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                      static_cast<const T*>(a.k_pyr), static_cast<const T*>(a.v_pyr), a.level_map,
                      static_cast<T*>(a.o), a.lse, a.H, a.H_kv, a.N, a.nqb, a.nkb, a.L, total, per,
@@ -422,10 +464,11 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
 
 template <typename T>
 static hipError_t launch_attn_dtype(const AttnArgs& a, hipStream_t stream) {
+  // 64-row query blocks: four waves as two row groups x two key halves
   if (a.d == 128) {
-    return a.q_block == 128 ? launch_attn_t<T, 128, 4>(a, stream) : launch_attn_t<T, 128, 2>(a, stream);
+    return a.q_block == 128 ? launch_attn_t<T, 128, 4, 1>(a, stream) : launch_attn_t<T, 128, 4, 2>(a, stream);
   }
-  return a.q_block == 128 ? launch_attn_t<T, 64, 4>(a, stream) : launch_attn_t<T, 64, 2>(a, stream);
+  return a.q_block == 128 ? launch_attn_t<T, 64, 4, 1>(a, stream) : launch_attn_t<T, 64, 4, 2>(a, stream);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
