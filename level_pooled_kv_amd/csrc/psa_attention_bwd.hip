@@ -60,7 +60,10 @@ bwd_rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dout, const flo
 }
 
 // ------------------------------------------------------------------ dq (query-outer)
-template <typename T, int D, int NW>
+// KS = 2 (64-row query blocks): the NW = 4 waves are 2 row groups x 2 key halves of every
+// tile, and the two halves' dq^T are summed through LDS at the end (four waves per
+// workgroup keep two waves per SIMD).
+template <typename T, int D, int NW, int KS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                            const T* __restrict__ kp, const T* __restrict__ vp,
@@ -86,14 +89,16 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
   const int bh = item / nqb, qi = item - bh * nqb;
   const int b = bh / H, h = bh - b * H;
   const int bkv = b * H_kv + h / (H / H_kv);
-  const int q0 = qi * (32 * NW);
+  constexpr int RW = NW / KS;                 // row groups of 32 queries
+  const int q0 = qi * (32 * RW);
 
   const int8_t* lrow = level_map + (int64_t)item * nkb;
   if (wave == 0) build_tile_lists(lrow, nkb, L, N, causal ? q0 / 64 : nkb, blist, tdesc, s_tile);
 
   // Q and dO as B operands: lane (row = lane%32, half = lane/32) holds d = 16c + 8*half + 0..7
   const int half = lane >> 5, l32 = lane & 31;
-  const int my_row = q0 + 32 * wave + l32;
+  const int khalf = KS == 1 ? 0 : wave / RW;   // key half of every tile
+  const int my_row = q0 + 32 * (KS == 1 ? wave : wave % RW) + l32;
   bf16x8 qreg[C::kQc], doreg[C::kQc];
   {
     const int64_t roff = ((int64_t)bh * N + min(my_row, N - 1)) * D;
@@ -225,7 +230,8 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
     int zero;   // opaque: keeps the LDS address arithmetic in the loop (hoisted, it spilled)
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kbi = 0; kbi < 2 / KS; ++kbi) {
+      const int kb = kbi + (2 / KS) * khalf;
       f32x16 sacc, dpacc;
 #pragma unroll
       for (int x = 0; x < 16; ++x) sacc[x] = dpacc[x] = 0.f;
@@ -290,7 +296,25 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
     if (t + 1 < T_total) body(t + 1, P1{});
   }
 
-  if (my_row < N) {
+  if constexpr (KS == 2) {
+    // sum the two key halves: the khalf = 1 waves hand their dq^T over through LDS (the
+    // tile buffers are idle after the loop's last barrier)
+    float* xq = reinterpret_cast<float*>((wave % RW) == 0 ? K0 : K1);   // [tt][x][lane]
+    if (khalf == 1) {
+#pragma unroll
+      for (int tt = 0; tt < C::kDt; ++tt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) xq[(tt * 16 + x) * 64 + lane] = dqacc[tt][x];
+    }
+    __syncthreads();
+    if (khalf == 0) {
+#pragma unroll
+      for (int tt = 0; tt < C::kDt; ++tt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) dqacc[tt][x] += xq[(tt * 16 + x) * 64 + lane];
+    }
+  }
+  if (my_row < N && khalf == 0) {
     T* orow = dq + ((int64_t)bh * N + my_row) * D;
 #pragma unroll
     for (int tt = 0; tt < C::kDt; ++tt) {
@@ -640,7 +664,7 @@ static DkdvGeom dkdv_geometry(const BwdArgs& a) {
   return g;
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int KS>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   constexpr int E = io_traits<T>::per16, CPR = D / E;
   const T* q = static_cast<const T*>(a.q);
@@ -655,7 +679,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
   const int total = a.B * a.H * a.nqb;
   const int per = (total + 7) / 8;
-  hipLaunchKernelGGL((pyramid_attn_bwd_dq_kernel<T, D, NW>), dim3(8 * per), dim3(NW * 64), 0, stream, q,
+  hipLaunchKernelGGL((pyramid_attn_bwd_dq_kernel<T, D, NW, KS>), dim3(8 * per), dim3(NW * 64), 0, stream, q,
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<const T*>(a.k_pyr),
                      static_cast<const T*>(a.v_pyr), a.level_map, a.lse, a.Dr, dout, static_cast<T*>(a.dq), a.H,
                      a.H_kv, a.N, a.Npad, a.nqb, a.nkb, a.L, total, per, a.pyr_rows, a.rows[1], a.rows[2], cs, a.scale,
@@ -683,8 +707,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
 template <typename T>
 static hipError_t launch_bwd_dtype(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return a.q_block == 128 ? launch_bwd_t<T, 128, 4>(a, stream) : launch_bwd_t<T, 128, 2>(a, stream);
-  return a.q_block == 128 ? launch_bwd_t<T, 64, 4>(a, stream) : launch_bwd_t<T, 64, 2>(a, stream);
+  // 64-row query blocks: dq with four waves as two row groups x two key halves
+  if (a.d == 128) return a.q_block == 128 ? launch_bwd_t<T, 128, 4, 1>(a, stream) : launch_bwd_t<T, 128, 4, 2>(a, stream);
+  return a.q_block == 128 ? launch_bwd_t<T, 64, 4, 1>(a, stream) : launch_bwd_t<T, 64, 4, 2>(a, stream);
 }
 
 hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t stream) {
