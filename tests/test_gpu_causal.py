@@ -107,6 +107,7 @@ CASES = [
     ("dense prefix 226 N=1200 d64", 1200, 64, 128, 4, "bf16", 2, 2, (0.05, 0.2, 0.4, 0.6), None, 226),
     ("ranked N=3000 d128", 3000, 128, 128, 4, "bf16", 2, 2, None, (0.1, 0.3, 0.5, 0.7), 0),
     ("ranked top-k N=2500 d64 bq64", 2500, 64, 64, 1, "bf16", 2, 2, None, (0.25,), 0),
+    ("N=1301 d128 bq64 gqa", 1301, 128, 64, 4, "bf16", 4, 2, (0.3, 0.55, 0.75, 0.9), None, 0),
 ]
 
 
@@ -122,6 +123,7 @@ ARBITRARY = [
     # label, N, d, q_block, dtype, H, H_kv
     ("arbitrary maps N=1000 d128 bq128", 1000, 128, 128, "bf16", 2, 2),
     ("arbitrary maps N=777 d64 bq64 f32", 777, 64, 64, "f32", 2, 1),
+    ("arbitrary maps N=1301 d128 bq64 gqa", 1301, 128, 64, "bf16", 4, 2),
 ]
 
 
