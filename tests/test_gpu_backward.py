@@ -78,6 +78,8 @@ CASES = [
     ("N=900 d128 f32 L=3", 900, 128, 128, 3, "f32", 2, 1, False),
     ("causal N=1000 d128 bq128", 1000, 128, 128, 4, "bf16", 2, 2, True),
     ("causal N=777 d64 bq64 f32", 777, 64, 64, 4, "f32", 2, 1, True),
+    ("N=1301 d128 bq64 gqa", 1301, 128, 64, 4, "bf16", 4, 2, False),
+    ("causal N=1301 d128 bq64 gqa", 1301, 128, 64, 4, "bf16", 4, 2, True),
 ]
 
 
