@@ -336,7 +336,8 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
 // ------------------------------------------------------------------ dK, dV (key-outer)
 struct DkdvGeom {
   int tiles[kMaxLevels];     // 64-row tiles of level l: ceil(rows_l / 64)
-  int first[kMaxLevels + 1]; // first tile index of level l among one head's tiles; first[L] = total
+  int first[kMaxLevels + 1]; // first tile index of level l among one head's tiles (coarsest level
+                             // first); first[kMaxLevels] = tiles per head
   int rows[kMaxLevels];      // rows of level l (level 0: N)
   int woff[kMaxLevels];      // row offset of level l in a head's float32 gradient rows
   int poff[kMaxLevels];      // row offset of level l in the pyramid (l >= 1)
@@ -371,13 +372,15 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
   const int bid = blockIdx.x;
   const int item = (bid & 7) * per_xcd + (bid >> 3);
   if (item >= total_items) return;
-  const int tiles_head = geo.first[L];
+  const int tiles_head = geo.first[kMaxLevels];
   const int bg = item / tiles_head;
   const int rem = item - bg * tiles_head;
-  int lvl = 0;
+  // a head's tiles run from the coarsest level down: the coarse tiles, kept by many
+  // query blocks, are the long items and start first
+  int lvl = L - 1;
 #pragma unroll
-  for (int l = 1; l < kMaxLevels; ++l)
-    if (l < L && rem >= geo.first[l]) lvl = l;
+  for (int l = kMaxLevels - 2; l >= 0; --l)
+    if (l < L - 1 && rem >= geo.first[l]) lvl = l;
   const int kt = rem - geo.first[lvl];
   const int b = bg / H_kv, g = bg - b * H_kv;
   const int G = H / H_kv;
@@ -648,19 +651,22 @@ bwd_unpool_kernel(const float* __restrict__ dkw, const float* __restrict__ dvw, 
 // ------------------------------------------------------------------ launch
 static DkdvGeom dkdv_geometry(const BwdArgs& a) {
   DkdvGeom g{};
-  int first = 0, woff = 0;
+  int woff = 0;
   for (int l = 0; l < kMaxLevels; ++l) {
     const int rows = l < a.L ? (a.N + (1 << l) - 1) >> l : 0;
     g.rows[l] = rows;
     g.tiles[l] = (rows + 63) / 64;
-    g.first[l] = first;
-    first += g.tiles[l];
     g.woff[l] = woff;
     woff += rows;
     g.poff[l] = l >= 1 ? a.off[l] : 0;
   }
+  int first = 0;   // levels L-1, ..., 0 in that order
+  for (int l = a.L - 1; l >= 0; --l) {
+    g.first[l] = first;
+    first += g.tiles[l];
+  }
+  for (int l = a.L; l < kMaxLevels; ++l) g.first[l] = first;
   g.first[kMaxLevels] = first;
-  for (int l = a.L; l <= kMaxLevels; ++l) g.first[l] = first;   // first[L] = tiles per head
   return g;
 }
 
