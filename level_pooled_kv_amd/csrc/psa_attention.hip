@@ -282,6 +282,9 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     if constexpr (kDirect) st = stage_addr(min(t + 1, T_total - 1), PN{});
     else if (t + 1 < T_total) issue_tile(t + 1, PN{});
     constexpr int SK = KB * C::kQc / BPW, SV = 2 * KB * C::kDt / BPW;   // MFMAs per interleaved load
+    // the compiler's interleaving of LDS reads with the matrix ops of this region
+    // (about 1% on the 32760-token layer, interleaved A/B)
+    __builtin_amdgcn_iglp_opt(0);
     const TileInfo ti = tile_info(t);
     const int lvl = ti.lvl;
     const bool irr = ti.irr;
