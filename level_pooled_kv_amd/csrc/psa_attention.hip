@@ -201,7 +201,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   };
   // Direct-load path: the byte offsets of tile t's staged rows are computed up front
   // (with the tile's logit corrections when irregular), and the loads themselves are
-  // issued one at a time between the MFMAs of the current tile, so no wave stalls
+  // issued one at a time between the S-product MFMAs of the current tile, so no wave stalls
   // behind a burst of loads queued at the CU's load path.
   struct Stage { const char* kb; const char* vb; uint32_t koff[BPW], voff[BPW]; };
   auto stage_addr = [&](int t, auto P) {
@@ -281,7 +281,9 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     Stage st{};
     if constexpr (kDirect) st = stage_addr(min(t + 1, T_total - 1), PN{});
     else if (t + 1 < T_total) issue_tile(t + 1, PN{});
-    constexpr int SK = KB * C::kQc / BPW, SV = 2 * KB * C::kDt / BPW;   // MFMAs per interleaved load
+    // the next tile's K and V loads go out one per SK S-product MFMAs, K first: issued
+    // early, they have the softmax and the P.V products to land before the tile's wait
+    constexpr int SK = KB * C::kQc / (2 * BPW);
     // the compiler's interleaving of LDS reads with the matrix ops of this region
     // (about 1% on the 32760-token layer, interleaved A/B)
     __builtin_amdgcn_iglp_opt(0);
@@ -306,7 +308,11 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sacc[kb], 0, 0, 0);
         if constexpr (kDirect) {
           const int j = kb * C::kQc + c;
-          if ((j + 1) % SK == 0) dma_k(st, j / SK, PN{});
+          if ((j + 1) % SK == 0) {
+            const int u = j / SK;
+            if (u < BPW) dma_k(st, u, PN{});
+            else dma_v(st, u - BPW, PN{});
+          }
         }
       }
     }
@@ -380,10 +386,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         }
         const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, preg[c], oacc[tt], 0, 0, 0);
-        if constexpr (kDirect) {
-          const int j = c * C::kDt + tt;
-          if ((j + 1) % SV == 0) dma_v(st, j / SV, PN{});
-        }
+
       }
     }
 
