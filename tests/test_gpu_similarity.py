@@ -102,6 +102,35 @@ def test_similarity_and_cap_small(psa, case):
     say(f"{label}: ok (sim max err {err.max():.1e}, {changed} levels capped, {n} near-threshold differences)")
 
 
+def test_similarity_cap_causal(psa):
+    # the cap under causal use: diagonal blocks stay at level 0, invisible ones pruned,
+    # and attention on the capped map matches the causal oracle
+    N, d, bq, L, thr = 1500, 128, 128, 4, 0.7
+    q, k, v = random_qkv(77, 1, 2, 2, N, d, "bf16")
+    k = o.round_to_bf16(structured_keys(k, 3))
+    s = 1.0 / math.sqrt(d)
+    prob = psa.Problem(B=1, H=2, H_kv=2, N=N, d=d, q_block=bq, num_levels=L, dtype="bf16", causal=True)
+    say(f"causal similarity cap, threshold {thr}")
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    kp, vp, kb, ksim = psa.psa_build_pyramid_sim(prob, kd, vd)
+    lev, _ = psa.psa_estimate_mask(prob, qd, kb, (0.3, 0.55, 0.75, 0.9))
+    lev_in = lev.cpu().numpy()
+    capped = psa.psa_apply_similarity_cap(prob, ksim, thr, lev.clone())
+    torch.cuda.synchronize()
+    sim_ora = o.key_similarity(k, 64, L)
+    cap_g = capped.cpu().numpy()
+    check_cap(cap_g, lev_in, sim_ora, thr, 2, "causal cap")
+    vis, diag = o.causal_blocks(N, bq, 64)
+    assert np.all(cap_g[..., ~vis] == -1) and np.all(cap_g[..., diag] == 0)
+    out, _ = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, capped)
+    torch.cuda.synchronize()
+    kpyr = [np.asarray(k, np.float64)] + [o.round_to_io(a, "bf16") for a in o.build_pyramid(k, L)[1:]]
+    vpyr = [np.asarray(v, np.float64)] + [o.round_to_io(a, "bf16") for a in o.build_pyramid(v, L)[1:]]
+    O, _ = o.pyramid_attention(q, kpyr, vpyr, cap_g, bq, 64, s, causal=True)
+    check_attention(to_host(out), O, "causal cap attention")
+    say("causal similarity cap: ok")
+
+
 def test_cap_extremes(psa):
     q, k, v = random_qkv(5, 1, 2, 2, 900, 128, "bf16")
     prob = psa.Problem(B=1, H=2, H_kv=2, N=900, d=128, q_block=128, num_levels=4, dtype="bf16")
