@@ -14,12 +14,14 @@
 //  * pyramid_attn_bwd_dq_kernel: dq, one workgroup per (batch, head, query block) over
 //    the same level-homogeneous 64-row key tiles as the forward (S^T = K Q^T and
 //    dP^T = V dO^T on the matrix cores, dq^T += K^T dS^T with K^T read by LDS
-//    transposing loads). No atomics.
+//    transposing loads; 64-row query blocks split each tile's keys between two wave
+//    pairs and sum their dq^T at the end). No atomics.
 //  * pyramid_attn_bwd_dkdv_kernel: dK and dV of the pooled rows, key-outer: one
 //    workgroup per (batch, KV head, level, 64-row tile of that level) walks every
 //    (query head of the group, query block) that keeps any block of the tile at that
 //    level (blocks it does not keep are masked per key), stages the query block's Q
-//    and dO in LDS and accumulates dK^T and dV^T in registers. No atomics; each
+//    and dO in LDS and accumulates dK^T and dV^T in registers. A head's tiles are
+//    dispatched from the coarsest level down (the long items first). No atomics; each
 //    pooled row is written once (float32, zero if unused).
 //  * bwd_unpool_kernel: dk_t = dK^0_t + sum_l dK^l_{t >> l} / c, in the I/O dtype.
 #include "psa_attn_common.h"
