@@ -166,3 +166,21 @@ def test_backward_full_workload_sampled(psa):
         check_grad(dk_g[:, h:h + 1, t0:t1], ref["dk"][:, :, t0:t1], w.dtype, f"dk head {h} block {j}")
         check_grad(dv_g[:, h:h + 1, t0:t1], ref["dv"][:, :, t0:t1], w.dtype, f"dv head {h} block {j}")
     say(f"{w.name}: ok")
+
+
+def test_backward_deterministic(psa):
+    # no atomics anywhere in the backward: two calls give bit-identical gradients
+    N, d = 3000, 128
+    q, k, v = random_qkv(61, 1, 4, 2, N, d, "bf16")
+    prob = psa.Problem(B=1, H=4, H_kv=2, N=N, d=d, q_block=128, num_levels=4, dtype="bf16")
+    say("backward determinism, N=3000 gqa")
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    dod = to_device(o.round_to_bf16(np.random.default_rng(2).standard_normal(q.shape)), "bf16")
+    kp, vp, kbar = psa.psa_build_pyramid(prob, kd, vd)
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, (0.3, 0.55, 0.75, 0.9))
+    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lev, want_lse=True)
+    g1 = psa.psa_attention_bwd(prob, qd, kd, vd, kp, vp, lev, out, lse, dod)
+    g2 = psa.psa_attention_bwd(prob, qd, kd, vd, kp, vp, lev, out, lse, dod)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
