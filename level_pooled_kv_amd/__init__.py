@@ -127,7 +127,12 @@ class Problem:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor for the C ABI (after every shape and dtype check of the call)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a tensor on a HIP device, got one on {t.device}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -136,9 +141,10 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _need(t: torch.Tensor, name: str, shape, dtype):
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name}: expected contiguous {dtype} device tensor of shape {tuple(shape)}, "
-                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+    """Shape, dtype and layout check (the device is checked when the pointer is taken)."""
+    if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        got = "None" if t is None else f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}"
+        raise ValueError(f"{name}: expected contiguous {dtype} tensor of shape {tuple(shape)}, got {got}")
 
 
 def _pyramid_buffers(prob: Problem, k, v, k_pyr, v_pyr, k_bar):
@@ -256,10 +262,16 @@ def psa_attention_fwd(prob: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.
     _need(k, "k", (prob.B, prob.H_kv, prob.N, prob.d), dt)
     _need(v, "v", (prob.B, prob.H_kv, prob.N, prob.d), dt)
     _need(level_map, "level_map", (prob.B, prob.H, prob.nqb, prob.nkb), torch.int8)
+    if prob.num_levels > 1:
+        for t, name in ((k_pyr, "k_pyr"), (v_pyr, "v_pyr")):
+            _need(t, name, (prob.B, prob.H_kv, prob.pyramid_rows, prob.d), dt)
     if o is None:
         o = torch.empty_like(q)
+    _need(o, "o", (prob.B, prob.H, prob.N, prob.d), dt)
     if lse is None and want_lse:
         lse = torch.empty((prob.B, prob.H, prob.N), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", (prob.B, prob.H, prob.N), torch.float32)
     _check(_lib.psa_attention_fwd(ctypes.byref(prob.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(k_pyr), _ptr(v_pyr),
                                   _ptr(level_map), _ptr(o), _ptr(lse), None, 0, _stream(stream)))
     return o, lse

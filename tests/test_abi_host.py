@@ -186,3 +186,37 @@ def test_status_strings(psa):
     assert names == ["PSA_OK", "PSA_ERR_INVALID_ARGUMENT", "PSA_ERR_UNSUPPORTED",
                      "PSA_ERR_WORKSPACE_TOO_SMALL", "PSA_ERR_HIP"]
     assert psa.status_string(99) == "PSA_ERR_UNKNOWN"
+
+
+def test_binding_checks_attention_buffers(psa):
+    """The binding rejects pyramid, output and lse buffers of the wrong shape or dtype before
+    any pointer reaches the library (host tensors: the device check comes last)."""
+    import torch
+    p = prob(psa, B=1, H=2, H_kv=1, N=300, d=64, q_block=64)
+    bf = torch.bfloat16
+    q = torch.zeros((1, 2, 300, 64), dtype=bf)
+    k = torch.zeros((1, 1, 300, 64), dtype=bf)
+    lm = torch.zeros((1, 2, p.nqb, p.nkb), dtype=torch.int8)
+    R = p.pyramid_rows
+    kp = torch.zeros((1, 1, R, 64), dtype=bf)
+    good = dict(k_pyr=kp, v_pyr=kp.clone(), o=torch.zeros_like(q), lse=torch.zeros((1, 2, 300)))
+    bad = {
+        "k_pyr": [None, torch.zeros((1, 1, R - 1, 64), dtype=bf), torch.zeros((1, 1, R, 64))],
+        "v_pyr": [None, torch.zeros((1, 1, R, 128), dtype=bf)],
+        "o": [torch.zeros((1, 2, 300, 64)), torch.zeros((1, 2, 299, 64), dtype=bf),
+              torch.zeros((1, 2, 64, 300), dtype=bf).transpose(2, 3)],
+        "lse": [torch.zeros((1, 2, 300), dtype=bf), torch.zeros((1, 1, 300))],
+    }
+    for name, cases in bad.items():
+        for t in cases:
+            kw = dict(good)
+            kw[name] = t
+            with pytest.raises(ValueError, match=name):
+                psa.psa_attention_fwd(p, q, k, k, kw["k_pyr"], kw["v_pyr"], lm, o=kw["o"], lse=kw["lse"])
+    # every shape right: only the device check is left, and it fails on host tensors
+    with pytest.raises(ValueError, match="HIP device"):
+        psa.psa_attention_fwd(p, q, k, k, good["k_pyr"], good["v_pyr"], lm, o=good["o"], lse=good["lse"])
+    # one level: the pyramid may be omitted
+    p1 = prob(psa, B=1, H=2, H_kv=1, N=300, d=64, q_block=64, num_levels=1)
+    with pytest.raises(ValueError, match="HIP device"):
+        psa.psa_attention_fwd(p1, q, k, k, None, None, lm)
