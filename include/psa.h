@@ -10,6 +10,7 @@
  *   psa_build_pyramid  — average-pooled K/V levels 1..L-1 and per-block mean keys
  *   psa_estimate_mask  — block importance and the threshold-based level map
  *   psa_estimate_mask_ranked — the same with a fixed share of ranked blocks per level
+ *   psa_estimate_mask_noalloc — psa_estimate_mask with a static workspace (allocates nothing)
  *   psa_build_pyramid_sim, psa_apply_similarity_cap — the cosine-similarity constraint
  *   psa_attention_fwd  — attention over mixed-resolution keys, one softmax
  *   psa_attention_bwd  — its gradients with respect to q, k and v
@@ -31,7 +32,9 @@
  *    library keeps no pointer after a call returns. Device pointers must be
  *    16-byte aligned. `thresholds` and `fractions` are host pointers.
  *  - Calls only enqueue kernels on `stream` and return without synchronising.
- *    The library holds no state and allocates no memory; calls are thread-safe.
+ *    The library allocates no memory and holds no state, except the static device
+ *    scratch of psa_estimate_mask_noalloc (see there); calls are thread-safe, but
+ *    overlapping psa_estimate_mask_noalloc calls on one device race on its scratch.
  *  - Arguments are checked before anything is launched: invalid values return
  *    PSA_ERR_INVALID_ARGUMENT, valid shapes outside the supported envelope
  *    PSA_ERR_UNSUPPORTED, a short workspace PSA_ERR_WORKSPACE_TOO_SMALL; a failed
@@ -184,6 +187,32 @@ psa_status_t psa_estimate_mask_ranked(const psa_problem_t* prob, const void* q, 
                                       const double* fractions, int32_t n_dense_prefix,
                                       int8_t* level_map, float* cmass_out,
                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Capacity, in bytes, of the library's static device scratch used by
+ * psa_estimate_mask_noalloc. */
+#define PSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * psa_estimate_mask for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation, kernels and results, with the workspace taken from a static device
+ * array of PSA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it
+ * runs on until the process ends. The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine. The caller still provides q, k_bar,
+ * level_map and cmass_out (nullable) as for psa_estimate_mask.
+ * The first call on a device looks up that device's copy of the array (with the
+ * device current); later calls reuse the address.
+ * Errors: as psa_estimate_mask; a problem whose workspace
+ * (psa_workspace_bytes(prob, PSA_WS_ESTIMATE_MASK)) exceeds the array returns
+ * PSA_ERR_WORKSPACE_TOO_SMALL before anything is launched.
+ * Every call on one device shares that device's array: calls that overlap in time on
+ * one device (several streams or threads) race on it and must be serialised by the
+ * caller. Nothing in the array needs to be zero on entry (every byte a kernel reads is
+ * written earlier in the same call).
+ */
+psa_status_t psa_estimate_mask_noalloc(const psa_problem_t* prob, const void* q, const float* k_bar,
+                                       const float* thresholds, int32_t n_dense_prefix,
+                                       int8_t* level_map, float* cmass_out, hipStream_t stream);
 
 /*
  * Step 3, attention over mixed-resolution keys with one softmax ("adaptive

@@ -33,7 +33,7 @@ PSA_WS_ESTIMATE_MASK, PSA_WS_ATTENTION_FWD, PSA_WS_ATTENTION_BWD = 0, 1, 2
 EXPORTED = (
     "psa_pyramid_rows", "psa_workspace_bytes", "psa_check_problem", "psa_build_pyramid", "psa_build_pyramid_sim",
     "psa_apply_similarity_cap",
-    "psa_estimate_mask", "psa_estimate_mask_ranked", "psa_attention_fwd", "psa_attention_bwd", "psa_status_string", "psa_last_error",
+    "psa_estimate_mask", "psa_estimate_mask_ranked", "psa_estimate_mask_noalloc", "psa_attention_fwd", "psa_attention_bwd", "psa_status_string", "psa_last_error",
 )
 
 
@@ -63,6 +63,10 @@ _lib.psa_estimate_mask.restype = _st
 _lib.psa_estimate_mask_ranked.argtypes = [_P, _vp, _vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int32, _vp,
                                           _vp, _vp, _sz, _vp]
 _lib.psa_estimate_mask_ranked.restype = _st
+_lib.psa_estimate_mask_noalloc.argtypes = [_P, _vp, _vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int32, _vp, _vp,
+                                           _vp]
+_lib.psa_estimate_mask_noalloc.restype = _st
+NOALLOC_SCRATCH_BYTES = 32 << 20     # PSA_NOALLOC_SCRATCH_BYTES
 _lib.psa_attention_bwd.argtypes = [_P] + [_vp] * 13 + [_sz, _vp]
 _lib.psa_attention_bwd.restype = _st
 _lib.psa_attention_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -235,6 +239,23 @@ def psa_estimate_mask(prob: Problem, q: torch.Tensor, k_bar: torch.Tensor, thres
     _check(_lib.psa_estimate_mask(ctypes.byref(prob.c()), _ptr(q), _ptr(k_bar), tau, int(n_dense_prefix),
                                   _ptr(level_map), _ptr(cmass), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return level_map, cmass
+
+
+def psa_estimate_mask_noalloc(prob: Problem, q: torch.Tensor, k_bar: torch.Tensor, thresholds: Sequence[float],
+                              n_dense_prefix: int, level_map: torch.Tensor, cmass: Optional[torch.Tensor] = None,
+                              stream=None):
+    """Step 2 with the library's static device scratch as workspace (the C call allocates
+    nothing; the caller passes every output). Returns (level_map, cmass or None)."""
+    _need(q, "q", (prob.B, prob.H, prob.N, prob.d), prob.torch_dtype)
+    _need(k_bar, "k_bar", (prob.B, prob.H_kv, prob.nkb, prob.d), torch.float32)
+    shape = (prob.B, prob.H, prob.nqb, prob.nkb)
+    _need(level_map, "level_map", shape, torch.int8)
+    if cmass is not None:
+        _need(cmass, "cmass", shape, torch.float32)
+    tau = _per_level(prob, thresholds, "thresholds", ctypes.c_float)
+    _check(_lib.psa_estimate_mask_noalloc(ctypes.byref(prob.c()), _ptr(q), _ptr(k_bar), tau, int(n_dense_prefix),
+                                          _ptr(level_map), _ptr(cmass), _stream(stream)))
     return level_map, cmass
 
 

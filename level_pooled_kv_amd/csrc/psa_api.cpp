@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "psa_launch.h"
 
 namespace {
@@ -202,12 +204,22 @@ psa_status_t psa_apply_similarity_cap(const psa_problem_t* prob, const float* k_
   return hip_status(psa::launch_similarity_cap(a, stream), "psa_apply_similarity_cap launch");
 }
 
-// Checks shared by both mask entry points, then the launch. Exactly one of tau and
-// fractions is non-NULL: the threshold rule or the ranked rule.
-static psa_status_t estimate_mask_common(const psa_problem_t* prob, const void* q, const float* k_bar,
-                                         int32_t n_dense_prefix, int8_t* level_map, float* cmass_out,
-                                         void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                         const float* tau, const double* fractions, const char* what) {
+static psa_status_t check_thresholds(const psa_problem_t* prob, const float* thresholds) {
+  if (!thresholds) return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds is NULL");
+  for (int l = 0; l < prob->num_levels; ++l) {
+    const float t = thresholds[l];
+    if (!(t >= 0.f && t <= 1.f))
+      return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds[%d] = %g is not in [0, 1]", l, (double)t);
+    if (l > 0 && t < thresholds[l - 1])
+      return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds must be nondecreasing (thresholds[%d] < thresholds[%d])",
+                  l, l - 1);
+  }
+  return PSA_OK;
+}
+
+// Pointer and prefix checks of the mask entry points (the workspace is checked separately).
+static psa_status_t check_mask_pointers(const psa_problem_t* prob, const void* q, const float* k_bar,
+                                        int32_t n_dense_prefix, const int8_t* level_map, const float* cmass_out) {
   REQUIRE_PTR(q, "q");
   REQUIRE_PTR(k_bar, "k_bar");
   REQUIRE_PTR(level_map, "level_map");
@@ -215,6 +227,17 @@ static psa_status_t estimate_mask_common(const psa_problem_t* prob, const void* 
     return fail(PSA_ERR_INVALID_ARGUMENT, "cmass_out is not 16-byte aligned");
   if (n_dense_prefix < 0 || n_dense_prefix > prob->N)
     return fail(PSA_ERR_INVALID_ARGUMENT, "n_dense_prefix %d not in [0, N]", n_dense_prefix);
+  return PSA_OK;
+}
+
+// Checks shared by both mask entry points, then the launch. Exactly one of tau and
+// fractions is non-NULL: the threshold rule or the ranked rule.
+static psa_status_t estimate_mask_common(const psa_problem_t* prob, const void* q, const float* k_bar,
+                                         int32_t n_dense_prefix, int8_t* level_map, float* cmass_out,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                         const float* tau, const double* fractions, const char* what) {
+  psa_status_t s = check_mask_pointers(prob, q, k_bar, n_dense_prefix, level_map, cmass_out);
+  if (s != PSA_OK) return s;
   const size_t need = mask_workspace(prob);
   if (workspace_bytes < need)
     return fail(PSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
@@ -249,17 +272,61 @@ psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const f
   clear_error();
   psa_status_t s = check_problem(prob);
   if (s != PSA_OK) return s;
-  if (!thresholds) return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds is NULL");
-  for (int l = 0; l < prob->num_levels; ++l) {
-    const float t = thresholds[l];
-    if (!(t >= 0.f && t <= 1.f))
-      return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds[%d] = %g is not in [0, 1]", l, (double)t);
-    if (l > 0 && t < thresholds[l - 1])
-      return fail(PSA_ERR_INVALID_ARGUMENT, "thresholds must be nondecreasing (thresholds[%d] < thresholds[%d])",
-                  l, l - 1);
-  }
+  s = check_thresholds(prob, thresholds);
+  if (s != PSA_OK) return s;
   return estimate_mask_common(prob, q, k_bar, n_dense_prefix, level_map, cmass_out, workspace, workspace_bytes,
                               stream, thresholds, nullptr, "psa_estimate_mask launch");
+}
+
+// Static workspace of psa_estimate_mask_noalloc: one copy per device, held until the
+// process ends. Host code never uses `scratch` itself (on the host the name is only a
+// stand-in for the symbol): each device's address comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and only that address reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[PSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+psa_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PSA_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(PSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PSA_OK;
+}
+}  // namespace
+
+psa_status_t psa_estimate_mask_noalloc(const psa_problem_t* prob, const void* q, const float* k_bar,
+                                       const float* thresholds, int32_t n_dense_prefix, int8_t* level_map,
+                                       float* cmass_out, hipStream_t stream) {
+  clear_error();
+  psa_status_t s = check_problem(prob);
+  if (s != PSA_OK) return s;
+  s = check_thresholds(prob, thresholds);
+  if (s != PSA_OK) return s;
+  s = check_mask_pointers(prob, q, k_bar, n_dense_prefix, level_map, cmass_out);
+  if (s != PSA_OK) return s;
+  const size_t need = mask_workspace(prob);
+  if (need > PSA_NOALLOC_SCRATCH_BYTES)
+    return fail(PSA_ERR_WORKSPACE_TOO_SMALL,
+                "psa_estimate_mask_noalloc: the problem needs %zu bytes of workspace, the static scratch holds %zu",
+                need, (size_t)PSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != PSA_OK) return s;
+  return estimate_mask_common(prob, q, k_bar, n_dense_prefix, level_map, cmass_out, ws, PSA_NOALLOC_SCRATCH_BYTES,
+                              stream, thresholds, nullptr, "psa_estimate_mask_noalloc launch");
 }
 
 psa_status_t psa_estimate_mask_ranked(const psa_problem_t* prob, const void* q, const float* k_bar,

@@ -220,3 +220,22 @@ def test_binding_checks_attention_buffers(psa):
     p1 = prob(psa, B=1, H=2, H_kv=1, N=300, d=64, q_block=64, num_levels=1)
     with pytest.raises(ValueError, match="HIP device"):
         psa.psa_attention_fwd(p1, q, k, k, None, None, lm)
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch(psa):
+    """psa_estimate_mask_noalloc refuses, before anything else happens, a problem whose mask
+    workspace exceeds the static scratch (the 75600-token, 40-head layer needs about 205 MB)."""
+    f = psa.lib.psa_estimate_mask_noalloc
+    big = prob(psa, H=40, H_kv=40, N=75600)
+    need = big.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
+    assert need > psa.NOALLOC_SCRATCH_BYTES
+    c = big.c()
+    assert f(ctypes.byref(c), FAKE, FAKE, tau(0.1, 0.2, 0.3, 0.4), 0, FAKE, None, None) == 3
+    assert "static scratch" in psa.last_error() and str(need) in psa.last_error()
+    # argument errors come first, as in psa_estimate_mask
+    small = prob(psa).c()
+    assert f(ctypes.byref(small), FAKE, FAKE, tau(0.3, 0.2, 0.4, 0.5), 0, FAKE, None, None) == 1
+    assert f(ctypes.byref(small), None, FAKE, tau(0.1, 0.2, 0.3, 0.4), 0, FAKE, None, None) == 1
+    assert f(ctypes.byref(small), FAKE, FAKE, tau(0.1, 0.2, 0.3, 0.4), -1, FAKE, None, None) == 1
+    # the bench workload fits
+    assert prob(psa).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK) <= psa.NOALLOC_SCRATCH_BYTES
