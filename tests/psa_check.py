@@ -18,6 +18,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from tests.oracle_heads import lse_tolerance  # noqa: F401  (re-exported for the GPU tests)
+
 PYR_REL_L2 = 1e-3
 KBAR_TOL = 1e-5
 MASK_C_TOL = 1e-5
@@ -167,24 +169,6 @@ def check_cmass(gpu_C: np.ndarray, ora: dict, label: str = ""):
     return len(far)
 
 
-def lse_tolerance(q: np.ndarray, k: np.ndarray, scale: float, dtype: str) -> np.ndarray:
-    """Per-row bound on |lse_gpu - lse_oracle| ([B, H, N]).
-
-    bf16 I/O: the matrix cores multiply the exact bf16 inputs and accumulate in float32,
-    so only float32 accumulation error remains (1e-3 is generous). float32 I/O: q and k are
-    rounded to bf16 first, so every product q_c*k_c carries a relative error below 2^-8 and
-    every logit of row r moves by at most 2^-8 * scale * sum_c |q_rc| * max_t |k_tc|;
-    the log-sum-exp moves by at most the largest logit change."""
-    B, H, N, d = q.shape
-    tol = np.full((B, H, N), 1e-3)
-    if dtype == "f32":
-        H_kv = k.shape[1]
-        kmax = np.abs(k).max(axis=2)                                   # [B, H_kv, d]
-        kmax_h = np.repeat(kmax, H // H_kv, axis=1)                    # [B, H, d]
-        tol += 2.0 ** -8 * scale * np.einsum("bhnd,bhd->bhn", np.abs(q), kmax_h)
-    return tol
-
-
 def check_attention(o_gpu: np.ndarray, o_ora: np.ndarray, label: str = "", rows=None):
     """Compare O on the rows the oracle computed (non-NaN rows of o_ora, or `rows` mask)."""
     sel = ~np.isnan(o_ora[..., 0]) if rows is None else rows
@@ -195,3 +179,110 @@ def check_attention(o_gpu: np.ndarray, o_ora: np.ndarray, label: str = "", rows=
     mx, mean = float(err.max()), float(err.mean())
     assert mx <= ATT_MAX_ABS and mean <= ATT_MEAN_ABS, (label, mx, mean)
     return mx, mean
+
+
+# ------------------------------------------------------------------------------ backward bounds
+
+BF16_HALF_ULP = 2.0 ** -9      # relative rounding error of a bf16 value (8 significant bits)
+F32_UNIT = 2.0 ** -24          # relative rounding error of one float32 operation
+
+
+def backward_bounds(q, k, v, L, level_map, q_block, scale, dO, dtype, causal=False):
+    """Element-wise bounds on |gpu - oracle| for dq, dk, dv and the per-level pooled
+    gradients of psa_attention_bwd, derived from the roundings the kernels make.
+
+    Per query row r and pooled key p (P = softmax weight, dP = <dO_r, V_p>, D = <dO_r, O_r>,
+    dA = P (dP - D), e = 2^-9 the relative error of a bf16 rounding, u = 2^-24 of a float32
+    operation):
+      * the forward's O carries |dO| <= e |O| (its bf16 rounding) + e sum_p P |V_p| (P is
+        rounded to bf16 for the P.V product), so D is off by dD <= <|dO_r|, that bound>;
+      * dP is a float32 sum of d exact bf16 products: ddP <= d u <|dO_r|, |V_p|>;
+      * dA is computed in float32 and rounded to bf16: ddA <= e |dA| + P (dD + ddP)
+        (+ the effect of an error in P: relative 1e-6 for bf16 I/O, where the logits are
+        float32 sums of exact products and lse comes from the forward; for float32 I/O q and
+        k are rounded to bf16 first, which moves a logit by up to eps = 2^-8 scale <|q_r|,|K_p|>
+        and lse by up to the row's largest eps, so P moves by a factor up to e^(eps+max eps));
+      * dq_r = scale sum_p dA K_p, dK_p = scale sum_r dA q_r, dV_p = sum_r P dO_r (P rounded
+        to bf16: e P |dO_r|), each a float32 sum of n terms: + n u of its absolute sum; float32
+        I/O also rounds K, q and dO to bf16 (+ e of the absolute sum);
+      * a pooled row passes 1/c of its gradient to each of its c tokens (nonnegative weights:
+        the bounds add the same way), and bf16 outputs add their own rounding, e |g|.
+    Returns a dict with bounds "dq", "dk", "dv" [like the gradients] and "dk_levels",
+    "dv_levels" (per level, before the 1/c spread; float32 in the library's workspace)."""
+    from oracle import psa_oracle as o
+    e, u = BF16_HALF_ULP, F32_UNIT
+    f32 = dtype == "f32"
+    q = np.asarray(q, np.float64)
+    dO = np.asarray(dO, np.float64)
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    kp = [np.asarray(k, np.float64)] + [o.round_to_io(x, dtype) for x in o.build_pyramid(k, L)[1:]]
+    vp = [np.asarray(v, np.float64)] + [o.round_to_io(x, dtype) for x in o.build_pyramid(v, L)[1:]]
+    O, LSE = o.pyramid_attention(q, kp, vp, level_map, q_block, 64, scale, causal=causal)
+    bq = np.zeros_like(q)
+    bkl = [np.zeros_like(x) for x in kp]
+    bvl = [np.zeros_like(x) for x in vp]
+    nqb = -(-N // q_block)
+    n_rows_k = (H // H_kv) * N          # terms summed into one pooled key's gradient, at most
+    ext = e if f32 else 0.0
+    for b in range(B):
+        for h in range(H):
+            g = o.kv_head_of(h, H, H_kv)
+            for i in range(nqb):
+                keys, vals, logc, last, idx = o.gather_keys(level_map[b, h, i], N, 64, [x[b, g] for x in kp],
+                                                            [x[b, g] for x in vp], with_last=True, with_index=True)
+                if keys.shape[0] == 0:
+                    continue
+                r0, r1 = i * q_block, min((i + 1) * q_block, N)
+                qr, dOr, Or = q[b, h, r0:r1], dO[b, h, r0:r1], O[b, h, r0:r1]
+                a = scale * (qr @ keys.T) + logc[None, :]
+                if causal:
+                    seen = last[None, :] <= np.arange(r0, r1)[:, None]
+                    a = np.where(seen, a, -np.inf)
+                fin = np.isfinite(LSE[b, h, r0:r1])[:, None]
+                P = np.where(fin, np.exp(a - np.where(fin, LSE[b, h, r0:r1][:, None], 0.0)), 0.0)
+                dP = dOr @ vals.T
+                D = np.sum(dOr * Or, axis=1, keepdims=True)
+                dA = P * (dP - D)
+                aq, ak, av, ado = np.abs(qr), np.abs(keys), np.abs(vals), np.abs(dOr)
+                fwd_err = e * np.abs(Or) + e * (P @ av)
+                dD = np.sum(ado * fwd_err, axis=1, keepdims=True)
+                ddP = (d * u + 2 * ext) * (ado @ av.T)
+                if f32:
+                    eps = scale * 2.0 ** -8 * (aq @ ak.T)
+                    prel = np.expm1(eps + eps.max(axis=1, keepdims=True))
+                else:
+                    prel = 1e-6
+                ddA = e * np.abs(dA) + P * (dD + ddP) + prel * P * np.abs(dP - D)
+                adA = np.abs(dA)
+                n = keys.shape[0]
+                bq[b, h, r0:r1] = scale * (ddA @ ak) + scale * (n * u + ext) * (adA @ ak)
+                bK = scale * (ddA.T @ aq) + scale * (n_rows_k * u + ext) * (adA.T @ aq)
+                bV = (e + n_rows_k * u + ext) * (P.T @ ado) + (prel * P).T @ ado
+                for l in range(L):
+                    sel = idx[:, 0] == l
+                    np.add.at(bkl[l][b, g], idx[sel, 1], bK[sel])
+                    np.add.at(bvl[l][b, g], idx[sel, 1], bV[sel])
+    bk, bv = bkl[0].copy(), bvl[0].copy()
+    for l in range(1, L):
+        c = o.pool_counts(N, l).astype(np.float64)[:, None]
+        up = np.arange(N) >> l
+        bk += (bkl[l] / c)[:, :, up]
+        bv += (bvl[l] / c)[:, :, up]
+    return {"dq": bq, "dk": bk, "dv": bv, "dk_levels": bkl, "dv_levels": bvl}
+
+
+def check_grad_bound(g, r, bound, label, out_dtype=None):
+    """|g - r| <= bound (+ the output's own bf16 rounding, e |r|, when out_dtype is bf16)
+    element by element, with an absolute floor of 1e-6 of the largest reference entry.
+    Returns the largest ratio of error to bound."""
+    assert np.all(np.isfinite(g)), (label, "non-finite gradient")
+    tol = bound + (BF16_HALF_ULP * np.abs(r) if out_dtype == "bf16" else 0.0)
+    tol = tol + 1e-6 * max(float(np.abs(r).max()), 1e-30)
+    err = np.abs(g - r)
+    bad = err > tol
+    if bad.any():
+        at = tuple(int(x) for x in np.argwhere(bad)[0])
+        raise AssertionError((label, f"{int(bad.sum())} elements beyond their bound", at, float(err[at]),
+                              float(tol[at]), float(r[at])))
+    return float((err / tol).max())

@@ -1,12 +1,13 @@
 """Parity of the attention backward (psa_attention_bwd, through the C ABI) with the
 float64 oracle on MI355X.
 
-Tolerance (derived, not fitted): the kernels round P and dA to bf16 for their matrix
-products (relative 2^-9 per element) and take D_r = <dO_r, O_r> from the bf16 output,
-so each gradient carries relative errors of about 2^-9 per term; summed with random
-signs that stays near 2^-9 of the gradient's L2 norm. The bar is 1e-2 of the L2 norm
-(bf16 I/O) and 2e-2 for float32 I/O, whose inputs are also rounded to bf16 on the way
-into the matrix cores, plus a max-abs bound of 5e-2 of the largest reference entry.
+Tolerance (derived, not fitted): every element of dq, dk, dv, and of the per-level
+pooled gradients the library keeps in its workspace before spreading them over the
+tokens, must lie within the bound tests.psa_check.backward_bounds derives from the
+kernels' roundings (P and dA rounded to bf16 for their products, D_r = <dO_r, O_r> from
+the bf16 output, float32 sums, bf16 outputs; float32 I/O also rounds its inputs to bf16
+on the way into the matrix cores). As a whole-tensor sanity bound the relative L2 error
+must stay within 1e-2 (bf16 I/O) or 2e-2 (float32 I/O).
 Every case prints its name before touching the GPU.
 """
 import math
@@ -17,7 +18,7 @@ import torch
 
 from oracle import psa_oracle as o
 from synth import generate, get as get_workload, random_qkv
-from tests.psa_check import to_device, to_host
+from tests.psa_check import backward_bounds, check_grad_bound, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +38,8 @@ def say(msg):
 
 
 def check_grad(g, r, dtype, label):
+    """Relative L2 error within REL[dtype] (a whole-tensor sanity bound next to the
+    element-wise one)."""
     assert np.all(np.isfinite(g)), (label, "non-finite gradient")
     nr = np.linalg.norm(r.ravel())
     if nr == 0.0:   # e.g. a single key: dA = P (dP - D) vanishes up to float32 arithmetic
@@ -46,6 +49,24 @@ def check_grad(g, r, dtype, label):
     mx = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
     assert rel <= REL[dtype] and mx <= MAXREL, (label, float(rel), float(mx))
     return float(rel)
+
+
+def workspace_levels(ws, prob, which):
+    """Per-level float32 gradients of K (which = 0) or V (1) from the backward's workspace:
+    after two [B, H, N padded to 64] float32 arrays (each on a 256-byte boundary) come
+    [B, H_kv, N + pyramid rows, d] for K, then for V (level 0 rows first, then level 1, ...)."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    npad = -(-prob.N // 64) * 64
+    rows = prob.N + prob.pyramid_rows
+    off = 2 * r256(prob.B * prob.H * npad * 4) + which * r256(prob.B * prob.H_kv * rows * prob.d * 4)
+    n = prob.B * prob.H_kv * rows * prob.d
+    flat = ws[off:off + 4 * n].view(torch.float32).reshape(prob.B, prob.H_kv, rows, prob.d)
+    out, r0 = [], 0
+    for l in range(prob.num_levels):
+        R = -(-prob.N // 2 ** l)
+        out.append(to_host(flat[:, :, r0:r0 + R]))
+        r0 += R
+    return out
 
 
 def run_bwd(psa, label, q, k, v, lev, *, H, H_kv, d, q_block, L, dtype, causal=False, seed=0):
@@ -60,11 +81,20 @@ def run_bwd(psa, label, q, k, v, lev, *, H, H_kv, d, q_block, L, dtype, causal=F
     kp, vp, _ = psa.psa_build_pyramid(prob, kd, vd)
     lev_d = torch.from_numpy(lev).cuda()
     out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lev_d, want_lse=True)
-    dq, dk, dv = psa.psa_attention_bwd(prob, qd, kd, vd, kp, vp, lev_d, out, lse, dod)
+    ws = torch.empty(prob.workspace_bytes(psa.PSA_WS_ATTENTION_BWD), dtype=torch.uint8, device=qd.device)
+    dq, dk, dv = psa.psa_attention_bwd(prob, qd, kd, vd, kp, vp, lev_d, out, lse, dod, workspace=ws)
     torch.cuda.synchronize()
     ref = o.pyramid_attention_bwd(q, k, v, L, lev, q_block, 64, s, dO, io_dtype=dtype, causal=causal)
+    bnd = backward_bounds(q, k, v, L, lev, q_block, s, dO, dtype, causal=causal)
     rels = [check_grad(to_host(x), ref[n], dtype, f"{label} {n}") for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
-    say(f"{label}: ok (relative L2 error dq {rels[0]:.1e} dk {rels[1]:.1e} dv {rels[2]:.1e})")
+    worst = max(check_grad_bound(to_host(x), ref[n], bnd[n], f"{label} {n}", dtype)
+                for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
+    # the pooled gradients per level, before they are spread over the tokens
+    for which, name in ((0, "dk_levels"), (1, "dv_levels")):
+        for l, gl in enumerate(workspace_levels(ws, prob, which)):
+            worst = max(worst, check_grad_bound(gl, ref[name][l], bnd[name][l], f"{label} {name}[{l}]"))
+    say(f"{label}: ok (relative L2 error dq {rels[0]:.1e} dk {rels[1]:.1e} dv {rels[2]:.1e}; largest "
+        f"error / element bound {worst:.2f})")
     return ref
 
 
@@ -80,13 +110,17 @@ CASES = [
     ("causal N=777 d64 bq64 f32", 777, 64, 64, 4, "f32", 2, 1, True),
     ("N=1301 d128 bq64 gqa", 1301, 128, 64, 4, "bf16", 4, 2, False),
     ("causal N=1301 d128 bq64 gqa", 1301, 128, 64, 4, "bf16", 4, 2, True),
+    # batches (optional last field B)
+    ("B=2 ragged N=1500 d128 bq128 gqa", 1500, 128, 128, 4, "bf16", 6, 2, False, 2),
+    ("B=2 causal N=999 d64 bq64 gqa", 999, 64, 64, 4, "bf16", 4, 2, True, 2),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_backward_on_mask(psa, case):
-    label, N, d, bq, L, dtype, H, H_kv, causal = case
-    q, k, v = random_qkv(N + 11 * d + L, 1, H, H_kv, N, d, dtype)
+    label, N, d, bq, L, dtype, H, H_kv, causal, *rest = case
+    B = rest[0] if rest else 1
+    q, k, v = random_qkv(N + 11 * d + L + 1000 * (B - 1), B, H, H_kv, N, d, dtype)
     tau = (0.3, 0.55, 0.75, 0.9)[:L]
     lev = o.estimate_mask(q, k, bq, 64, tau, L, 1 / math.sqrt(d), causal=causal)["levels"]
     run_bwd(psa, label, q, k, v, lev, H=H, H_kv=H_kv, d=d, q_block=bq, L=L, dtype=dtype, causal=causal)
@@ -152,7 +186,10 @@ def test_backward_full_workload_sampled(psa):
         levs[:, :, i] = sub[:, :, 0]
         ref = o.pyramid_attention_bwd(qs, k[:, h:h + 1], v[:, h:h + 1], L, levs, w.q_block, 64, s, dOs,
                                       io_dtype=w.dtype)
+        bnd = backward_bounds(qs, k[:, h:h + 1], v[:, h:h + 1], L, levs, w.q_block, s, dOs, w.dtype)
         check_grad(dq_g[:, h:h + 1, r0:r1], ref["dq"][:, :, r0:r1], w.dtype, f"dq head {h} block {i}")
+        check_grad_bound(dq_g[:, h:h + 1, r0:r1], ref["dq"][:, :, r0:r1], bnd["dq"][:, :, r0:r1],
+                         f"dq head {h} block {i}", w.dtype)
     # dk, dv of sampled KV blocks: every query block of the head that keeps the block contributes
     for h, j in ((0, 3), (5, 400)):
         rows = [i for i in range(w.nqb) if lev_h[0, h, i, j] >= 0]
@@ -160,11 +197,15 @@ def test_backward_full_workload_sampled(psa):
         levs[0, 0, rows] = lev_h[0, h, rows]
         ref = o.pyramid_attention_bwd(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], L, levs, w.q_block, 64, s,
                                       dO[:, h:h + 1], io_dtype=w.dtype)
+        bnd = backward_bounds(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], L, levs, w.q_block, s,
+                              dO[:, h:h + 1], w.dtype)
         t0, t1 = 64 * j, 64 * j + 64
         # only block j's own tokens are compared: other blocks also get contributions from
         # query blocks outside the sample
-        check_grad(dk_g[:, h:h + 1, t0:t1], ref["dk"][:, :, t0:t1], w.dtype, f"dk head {h} block {j}")
-        check_grad(dv_g[:, h:h + 1, t0:t1], ref["dv"][:, :, t0:t1], w.dtype, f"dv head {h} block {j}")
+        for name, gg in (("dk", dk_g), ("dv", dv_g)):
+            check_grad(gg[:, h:h + 1, t0:t1], ref[name][:, :, t0:t1], w.dtype, f"{name} head {h} block {j}")
+            check_grad_bound(gg[:, h:h + 1, t0:t1], ref[name][:, :, t0:t1], bnd[name][:, :, t0:t1],
+                             f"{name} head {h} block {j}", w.dtype)
     say(f"{w.name}: ok")
 
 

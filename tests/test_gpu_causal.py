@@ -14,6 +14,7 @@ import torch
 
 from oracle import psa_oracle as o
 from synth import generate, get as get_workload, random_qkv
+from tests.oracle_heads import compare_heads
 from tests.psa_check import (check_attention, check_cmass, check_kbar, check_mask, check_mask_ranked,
                               lse_tolerance, to_device, to_host)
 
@@ -108,13 +109,17 @@ CASES = [
     ("ranked N=3000 d128", 3000, 128, 128, 4, "bf16", 2, 2, None, (0.1, 0.3, 0.5, 0.7), 0),
     ("ranked top-k N=2500 d64 bq64", 2500, 64, 64, 1, "bf16", 2, 2, None, (0.25,), 0),
     ("N=1301 d128 bq64 gqa", 1301, 128, 64, 4, "bf16", 4, 2, (0.3, 0.55, 0.75, 0.9), None, 0),
+    # batches (optional last field B)
+    ("B=2 ragged N=1500 d128 bq128 gqa", 1500, 128, 128, 4, "bf16", 6, 2, (0.3, 0.55, 0.75, 0.9), None, 0, 2),
+    ("B=2 ranked N=999 d64 bq64 gqa", 999, 64, 64, 4, "bf16", 4, 2, None, (0.1, 0.3, 0.5, 0.7), 0, 2),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_causal_small(psa, case):
-    label, N, d, bq, L, dtype, H, H_kv, tau, fr, ndp = case
-    q, k, v = random_qkv(N + 5 * d + L, 1, H, H_kv, N, d, dtype)
+    label, N, d, bq, L, dtype, H, H_kv, tau, fr, ndp, *rest = case
+    B = rest[0] if rest else 1
+    q, k, v = random_qkv(N + 5 * d + L + 1000 * (B - 1), B, H, H_kv, N, d, dtype)
     run_causal(psa, label, q, k, v, H=H, H_kv=H_kv, d=d, q_block=bq, L=L, dtype=dtype, tau=tau, fractions=fr,
                n_dense_prefix=ndp)
 
@@ -124,14 +129,16 @@ ARBITRARY = [
     ("arbitrary maps N=1000 d128 bq128", 1000, 128, 128, "bf16", 2, 2),
     ("arbitrary maps N=777 d64 bq64 f32", 777, 64, 64, "f32", 2, 1),
     ("arbitrary maps N=1301 d128 bq64 gqa", 1301, 128, 64, "bf16", 4, 2),
+    ("arbitrary maps B=2 N=1100 d128 bq128 gqa", 1100, 128, 128, "bf16", 4, 2, 2),
 ]
 
 
 @pytest.mark.parametrize("case", ARBITRARY, ids=[c[0] for c in ARBITRARY])
 def test_causal_attention_arbitrary_maps(psa, case):
     # pooled blocks on the diagonal and blocks in the future: the per-key causal rule alone
-    label, N, d, bq, dtype, H, H_kv = case
-    q, k, v = random_qkv(N + 17, 1, H, H_kv, N, d, dtype)
+    label, N, d, bq, dtype, H, H_kv, *rest = case
+    B = rest[0] if rest else 1
+    q, k, v = random_qkv(N + 17 + 1000 * (B - 1), B, H, H_kv, N, d, dtype)
     s = 1.0 / math.sqrt(d)
     prob = psa.Problem(B=1, H=H, H_kv=H_kv, N=N, d=d, q_block=bq, num_levels=4, dtype=dtype, causal=True)
     rng = np.random.default_rng(N)
@@ -227,24 +234,16 @@ def test_causal_full_workload(psa):
     C, lev_o = o.apply_causal(C, o.assign_levels(C, tau, L, 0, w.kv_block), w.N, w.q_block, w.kv_block)
     lev_g = lev.cpu().numpy()
     nacc = check_mask(lev_g, {"z": z, "p": p, "cmass": C, "levels": lev_o}, tau, L, 0, label=w.name)
-    say(f"{w.name}: GPU attention on the oracle's map, sampled query blocks")
-    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, torch.from_numpy(lev_o).cuda(), want_lse=True)
+    nfar = check_cmass(to_host(cm), {"z": z, "p": p, "cmass": C, "levels": lev_o}, w.name)
+    say(f"{w.name}: GPU attention on the oracle's map, every query block (outputs prefilled with NaN)")
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=qd.device)
+    psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, torch.from_numpy(lev_o).cuda(), o=out, lse=lse)
     torch.cuda.synchronize()
-    kpyr = [[x[:, g:g + 1].astype(np.float64)] + [o.round_to_io(a, w.dtype) for a in o.build_pyramid(x[:, g:g + 1], L)[1:]]
-            for x in (k,) for g in range(w.H_kv)]
-    vpyr = [[x[:, g:g + 1].astype(np.float64)] + [o.round_to_io(a, w.dtype) for a in o.build_pyramid(x[:, g:g + 1], L)[1:]]
-            for x in (v,) for g in range(w.H_kv)]
-    rng = np.random.default_rng(0)
-    items = {(0, 0, 0), (0, w.H - 1, w.nqb - 1)}
-    while len(items) < 8:
-        items.add((0, int(rng.integers(w.H)), int(rng.integers(w.nqb))))
-    for (b, h, i) in sorted(items):
-        g = o.kv_head_of(h, w.H, w.H_kv)
-        keys, vals, logc, last = o.gather_keys(lev_o[b, h, i], w.N, w.kv_block, [a[b, 0] for a in kpyr[g]],
-                                               [a[b, 0] for a in vpyr[g]], with_last=True)
-        r0, r1 = i * w.q_block, min((i + 1) * w.q_block, w.N)
-        allowed = last[None, :] <= np.arange(r0, r1)[:, None]
-        O_ref, lse_ref = o.attention_rows(q[b, h, r0:r1].astype(np.float64), keys, vals, logc, s, allowed)
-        check_attention(to_host(out[b, h, r0:r1]), O_ref, f"{w.name} item {(b, h, i)}", rows=np.ones(r1 - r0, bool))
-        assert np.all(np.abs(to_host(lse[b, h, r0:r1]) - lse_ref) <= 1e-3), (b, h, i)
+    assert bool(torch.isfinite(out).all()), (w.name, "output elements left unwritten or non-finite")
+    assert not bool(torch.isnan(lse).any()), (w.name, "lse rows left unwritten")
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    mx, mean, cnt = compare_heads(w.name, heads, lev_o, out.float().cpu().numpy(), lse.cpu().numpy(), say=say)
+    say(f"{w.name}: O over all {len(heads)} heads: max err {mx:.2e}, mean {mean:.2e}; cumulative masses "
+        f"outside 1e-5 inside the near-tie interval: {nfar}")
     say(f"{w.name}: ok (mask mismatches accepted: {nacc} of {lev_o.size})")

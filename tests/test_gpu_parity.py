@@ -1,9 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on MI355X.
 
 Every case prints its name before touching the GPU. Small cases compare every
-output element; the full-size workloads compare the pyramid, k_bar and the level
-map in full and the attention output on sampled query blocks (the oracle
-computes those one by one), in the same launch configuration the benchmark uses.
+output element; the full-size workloads compare the pyramid, k_bar, the level map
+and the cumulative mass in full, and the attention output of every query block of
+every head (of four spread heads for the 75600-token layer), in the same launch
+configuration the benchmark uses, with the output prefilled with NaN so that an
+unwritten element anywhere fails.
 """
 import math
 
@@ -13,6 +15,7 @@ import torch
 
 from oracle import psa_oracle as o
 from synth import get as get_workload, generate, random_qkv
+from tests.oracle_heads import compare_heads
 from tests.psa_check import (check_attention, check_cmass, check_kbar, check_mask, check_pyramid,
                               lse_tolerance, to_device, to_host)
 
@@ -109,13 +112,18 @@ RAGGED = [
     ("N=1536 d128 bq128 L=1", 1536, 128, 128, 1, "bf16", 2, 2),
     ("N=900 d128 bq128 f32", 900, 128, 128, 4, "f32", 2, 1),
     ("N=4100 d64 bq128 bf16", 4100, 64, 128, 4, "bf16", 3, 3),
+    # batches (optional last field B): the batch index in every kernel's addressing
+    ("B=2 ragged N=1500 d128 bq128 gqa", 1500, 128, 128, 4, "bf16", 6, 2, 2),
+    ("B=2 N=1000 d64 bq64 gqa f32", 1000, 64, 64, 4, "f32", 4, 1, 2),
+    ("B=3 ragged N=333 d128 bq64", 333, 128, 64, 4, "bf16", 2, 2, 3),
 ]
 
 
 @pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
 def test_ragged_shapes(psa, case):
-    label, N, d, bq, L, dtype, H, H_kv = case
-    q, k, v = random_qkv(N + d + L, 1, H, H_kv, N, d, dtype)
+    label, N, d, bq, L, dtype, H, H_kv, *rest = case
+    B = rest[0] if rest else 1
+    q, k, v = random_qkv(N + d + L + 1000 * (B - 1), B, H, H_kv, N, d, dtype)
     tau = (0.3, 0.55, 0.75, 0.9)[:L]
     run_small(psa, label, q, k, v, H=H, H_kv=H_kv, d=d, q_block=bq, L=L, dtype=dtype, tau=tau)
 
@@ -233,7 +241,13 @@ def test_deterministic(psa):
 
 # ------------------------------------------------------------------------------ full-size workloads
 
-def full_workload(psa, name, n_items=8, seed=0):
+# Heads whose every query block is compared with the oracle at full size: all heads, except
+# the 75600-token, 40-head layer, where the oracle takes a spread subset (first and last head
+# included); its pyramid, k_bar and level map are still compared in full.
+FULL_HEADS = {"wan14b": (0, 13, 26, 39)}
+
+
+def full_workload(psa, name):
     w = get_workload(name)
     tau = w.thresholds()
     L = w.num_levels
@@ -253,14 +267,12 @@ def full_workload(psa, name, n_items=8, seed=0):
     say(f"{name}: oracle pyramid per KV head")
     kbar_g = to_host(kbar)
     kbar_o = np.empty_like(kbar_g)
-    kp_levels = {}
     for g in range(w.H_kv):
         for name_t, x, dev in (("k", k, kp), ("v", v, vp)):
             lv = o.build_pyramid(x[:, g:g + 1], L)
-            lv_io = [x[:, g:g + 1].astype(np.float64)] + [o.round_to_io(a, w.dtype) for a in lv[1:]]
-            check_pyramid(gpu_levels_list(dev[:, g:g + 1], w.N, L), lv_io[1:], w.dtype, f"{name} {name_t} g={g}",
+            lv_io = [o.round_to_io(a, w.dtype) for a in lv[1:]]
+            check_pyramid(gpu_levels_list(dev[:, g:g + 1], w.N, L), lv_io, w.dtype, f"{name} {name_t} g={g}",
                           np.abs(x[:, g]).max())
-            kp_levels[(name_t, g)] = lv_io
         kbar_o[:, g] = o.block_means(k[:, g], w.kv_block)
     check_kbar(kbar_g, kbar_o, name)
 
@@ -271,31 +283,24 @@ def full_workload(psa, name, n_items=8, seed=0):
     C = o.cumulative_mass(z, p)
     lev_o = o.assign_levels(C, tau, L, w.n_dense_prefix, w.kv_block)
     lev_g = lev.cpu().numpy()
-    nacc = check_mask(lev_g, {"z": z, "p": p, "cmass": C, "levels": lev_o}, tau, L, w.n_dense_prefix,
-                      label=name)
+    ora_mask = {"z": z, "p": p, "cmass": C, "levels": lev_o}
+    nacc = check_mask(lev_g, ora_mask, tau, L, w.n_dense_prefix, label=name)
+    nfar = check_cmass(to_host(cm), ora_mask, name)
+    del q, k, v
 
-    say(f"{name}: GPU attention on the oracle's level map")
-    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, torch.from_numpy(lev_o).cuda(), want_lse=True)
+    say(f"{name}: GPU attention on the oracle's level map (outputs prefilled with NaN)")
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=qd.device)
+    psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, torch.from_numpy(lev_o).cuda(), o=out, lse=lse)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(seed)
-    items = {(0, w.H - 1, w.nqb - 1), (0, 0, 0)}
-    while len(items) < n_items:
-        items.add((int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.nqb))))
-    worst = 0.0
-    for (b, h, i) in sorted(items):
-        g = o.kv_head_of(h, w.H, w.H_kv)
-        keys, vals, logc = o.gather_keys(lev_o[b, h, i], w.N, w.kv_block,
-                                         [a[b, 0] for a in kp_levels[("k", g)]],
-                                         [a[b, 0] for a in kp_levels[("v", g)]])
-        r0, r1 = i * w.q_block, min((i + 1) * w.q_block, w.N)
-        O_ref, lse_ref = o.attention_rows(q[b, h, r0:r1].astype(np.float64), keys, vals, logc, s)
-        og = to_host(out[b, h, r0:r1])
-        mx, _ = check_attention(og, O_ref, f"{name} item {(b, h, i)}", rows=np.ones(r1 - r0, bool))
-        worst = max(worst, mx)
-        lg = to_host(lse[b, h, r0:r1])
-        tol = lse_tolerance(q[b:b + 1, h:h + 1, r0:r1], k[b:b + 1, g:g + 1], s, w.dtype)[0, 0]
-        assert np.all(np.abs(lg - lse_ref) <= tol), (name, (b, h, i), np.abs(lg - lse_ref).max())
-    say(f"{name}: ok (mask mismatches accepted: {nacc} of {lev_o.size}; O max err {worst:.2e})")
+    # every element of every head written (no row left at its NaN prefill)
+    assert bool(torch.isfinite(out).all()), (name, "output elements left unwritten or non-finite")
+    assert not bool(torch.isnan(lse).any()), (name, "lse rows left unwritten")
+    heads = [(b, h) for b in range(w.B) for h in FULL_HEADS.get(name, range(w.H))]
+    mx, mean, cnt = compare_heads(name, heads, lev_o, out.float().cpu().numpy(), lse.cpu().numpy(), say=say)
+    say(f"{name}: ok (mask mismatches accepted: {nacc} of {lev_o.size}, masses outside 1e-5 inside the "
+        f"near-tie interval: {nfar}; O over {len(heads)} whole heads: max err {mx:.2e}, mean {mean:.2e} "
+        f"over {cnt} elements)")
 
 
 @pytest.mark.parametrize("name", ["wan13b", "cogvx5b", "qwen7b", "wan14b"])

@@ -70,13 +70,17 @@ CASES = [
     ("N=1 d64", 1, 64, 128, 4, "bf16", 1, 1, (0.0, 1.0, 1.0, 1.0), 0),
     ("dense prefix 226 N=1200 d64", 1200, 64, 128, 4, "bf16", 2, 2, (0.1, 0.2, 0.4, 0.6), 226),
     ("keep nothing N=700", 700, 64, 128, 2, "bf16", 1, 1, (0.0, 0.0), 0),
+    # batches (optional last field B)
+    ("B=2 ragged N=1500 d128 bq128 gqa", 1500, 128, 128, 4, "bf16", 6, 2, (0.1, 0.3, 0.6, 0.9), 0, 2),
+    ("B=2 dense prefix 100 N=900 d64 bq64", 900, 64, 64, 4, "bf16", 2, 1, (0.05, 0.2, 0.4, 0.6), 100, 2),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_ranked_small(psa, case):
-    label, N, d, bq, L, dtype, H, H_kv, fr, ndp = case
-    q, k, v = random_qkv(N + 3 * d + L, 1, H, H_kv, N, d, dtype)
+    label, N, d, bq, L, dtype, H, H_kv, fr, ndp, *rest = case
+    B = rest[0] if rest else 1
+    q, k, v = random_qkv(N + 3 * d + L + 1000 * (B - 1), B, H, H_kv, N, d, dtype)
     ora, lev = run_ranked(psa, label, q, k, v, H=H, H_kv=H_kv, d=d, q_block=bq, L=L, dtype=dtype,
                           fractions=fr, n_dense_prefix=ndp)
     if fr[-1] == 0.0:

@@ -49,11 +49,12 @@ def structured_keys(k, seed):
     """Make some KV blocks similar (one direction plus small noise), keep others random."""
     r = np.random.default_rng(seed)
     B, Hkv, N, d = k.shape
-    for g in range(Hkv):
-        for j in range(0, -(-N // 64), 3):
-            lo, hi = 64 * j, min(64 * j + 64, N)
-            base = r.standard_normal(d)
-            k[0, g, lo:hi] = base + 0.05 * (j % 5) * r.standard_normal((hi - lo, d))
+    for b in range(B):
+        for g in range(Hkv):
+            for j in range(b % 2, -(-N // 64), 3):
+                lo, hi = 64 * j, min(64 * j + 64, N)
+                base = r.standard_normal(d)
+                k[b, g, lo:hi] = base + 0.05 * (j % 5) * r.standard_normal((hi - lo, d))
     return k
 
 
@@ -64,17 +65,20 @@ CASES = [
     ("N=1000 d64 bf16 bq64", 1000, 64, "bf16", 2, 1, 4, 64, 0.5),
     ("N=1500 d128 f32 L=2", 1500, 128, "f32", 2, 2, 2, 128, 0.8),
     ("N=70 d128 bf16", 70, 128, "bf16", 1, 1, 4, 128, 0.9),
+    # batches (optional last field B)
+    ("B=2 N=1500 d128 bf16 gqa", 1500, 128, "bf16", 6, 2, 4, 128, 0.7),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_similarity_and_cap_small(psa, case):
-    label, N, d, dtype, H, H_kv, L, bq, thr = case
-    q, k, v = random_qkv(N + 7 * d + L, 1, H, H_kv, N, d, dtype)
+    label, N, d, dtype, H, H_kv, L, bq, thr, *rest = case
+    B = rest[0] if rest else 1
+    q, k, v = random_qkv(N + 7 * d + L + 1000 * (B - 1), B, H, H_kv, N, d, dtype)
     k = structured_keys(k, N)
     k = o.round_to_bf16(k) if dtype == "bf16" else k.astype(np.float32).astype(np.float64)
     s = 1.0 / math.sqrt(d)
-    prob = psa.Problem(B=1, H=H, H_kv=H_kv, N=N, d=d, q_block=bq, num_levels=L, dtype=dtype)
+    prob = psa.Problem(B=B, H=H, H_kv=H_kv, N=N, d=d, q_block=bq, num_levels=L, dtype=dtype)
     say(f"{label}: similarity + cap, threshold {thr}")
     qd, kd, vd = to_device(q, dtype), to_device(k, dtype), to_device(v, dtype)
     kp0, vp0, kb0 = psa.psa_build_pyramid(prob, kd, vd)

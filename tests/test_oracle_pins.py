@@ -767,3 +767,88 @@ def test_worked_example():
         O, LSE = o.pyramid_attention(Q, kp, vp, m["levels"], bq, bk, s)
         np.testing.assert_allclose(O[0, 0, :, 0], o_ref, rtol=0, atol=1e-13)
         np.testing.assert_allclose(LSE[0, 0], lse_ref, rtol=0, atol=1e-13)
+
+
+def test_whole_head_comparison_catches_planted_errors():
+    """The whole-head parity helper of the GPU tests: the oracle's own output passes with zero
+    error; one element off by 0.05, a NaN, or a wrong lse are each caught."""
+    from synth import get as get_workload, generate
+    from tests.oracle_heads import compare_heads
+    w = get_workload("tiny")
+    q, k, v = generate(w, "q"), generate(w, "k"), generate(w, "v")
+    r = o.run_forward(q, k, v, w.q_block, w.kv_block, w.thresholds(), w.num_levels, w.scale, w.dtype)
+    lev, O, LSE = r["mask"]["levels"], r["O"], r["LSE"]
+    heads = [(0, 0), (0, 1)]
+    mx, mean, cnt = compare_heads("tiny", heads, lev, O.astype(np.float32), LSE.astype(np.float32), say=lambda m: None)
+    assert cnt == 2 * w.N * w.d and mx < 1e-5 and mean < 1e-6
+    bad = O.astype(np.float32).copy()
+    bad[0, 1, 1234, 5] += 0.05
+    with pytest.raises(AssertionError, match="heads off"):
+        compare_heads("tiny", heads, lev, bad, LSE.astype(np.float32), say=lambda m: None)
+    bad = O.astype(np.float32).copy()
+    bad[0, 0, 7, 0] = np.nan
+    with pytest.raises(AssertionError, match="heads off"):
+        compare_heads("tiny", heads, lev, bad, LSE.astype(np.float32), say=lambda m: None)
+    bad_lse = LSE.astype(np.float32).copy()
+    bad_lse[0, 1, 99] += 1.0     # float32 I/O: the bound allows the bf16 rounding of q and k
+    with pytest.raises(AssertionError, match="heads off"):
+        compare_heads("tiny", heads, lev, O.astype(np.float32), bad_lse, say=lambda m: None)
+
+
+def test_run_forward_worked_example():
+    """run_forward (the chain every GPU parity test and the smoke check call) on the
+    hand-derived worked example: pyramid, levels, O and LSE equal the closed forms, in
+    both I/O dtypes (every value of the example is exact in bf16)."""
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    N, bk, bq, L, s = ex["N"], ex["kv_block"], ex["q_block"], ex["num_levels"], ex["scale"]
+    K = np.array(ex["K"], float).reshape(1, 1, N, 1)
+    V = np.array(ex["V"], float).reshape(1, 1, N, 1)
+    Q = np.array(ex["Q"], float).reshape(1, 1, N, 1)
+    for io in ("f32", "bf16"):
+        for case in ex["cases"]:
+            r = o.run_forward(Q, K, V, bq, bk, case["thresholds"], L, s, io)
+            np.testing.assert_array_equal(r["kpyr"][0][0, 0, :, 0], ex["K"])
+            np.testing.assert_array_equal(r["kpyr"][1][0, 0, :, 0], ex["level1_K"])
+            np.testing.assert_array_equal(r["vpyr"][1][0, 0, :, 0], ex["level1_V"])
+            np.testing.assert_array_equal(r["mask"]["levels"][0, 0, 0], case["levels"])
+            w = [c * math.exp(a) for a, c in case["weights_exp_args"]]
+            o_ref = math.fsum(wi * vi for wi, vi in zip(w, case["values"])) / math.fsum(w)
+            np.testing.assert_allclose(r["O"][0, 0, :, 0], o_ref, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(r["LSE"][0, 0], math.log(math.fsum(w)), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("io,causal,ranked", [("bf16", False, False), ("f32", False, False),
+                                              ("bf16", True, False), ("bf16", False, True)])
+def test_run_forward_equals_its_steps(io, causal, ranked):
+    """run_forward against the step functions called one by one: the pyramid rounded to the
+    I/O dtype (level 0 = the inputs themselves), the mask of the chosen rule, and attention
+    over the rounded pyramid; GQA, a ragged tail and a partial pool group included."""
+    from synth import random_qkv
+    B, H, H_kv, N, d, bq, L = 2, 4, 2, 301, 8, 64, 4
+    q, k, v = random_qkv(515, B, H, H_kv, N, d, io)
+    k = k * 1.37          # pooled means no longer exact in bf16: the rounding step matters
+    v = v * 0.91
+    tau, fr, s = (0.2, 0.5, 0.7, 0.9), (0.1, 0.3, 0.6, 0.9), 0.3
+    r = o.run_forward(q, k, v, bq, 64, tau, L, s, io, n_dense_prefix=70,
+                      ranked_fractions=fr if ranked else None, causal=causal)
+    for name, x in (("kpyr", k), ("vpyr", v)):
+        lv = o.build_pyramid(x, L)
+        np.testing.assert_array_equal(r[name][0], np.asarray(x, np.float64))
+        for l in range(1, L):
+            np.testing.assert_array_equal(r[name][l], o.round_to_io(lv[l], io))
+            if io == "bf16":
+                assert not np.array_equal(r[name][l], lv[l])   # the rounding changed something
+    if ranked:
+        m = o.estimate_mask_ranked(q, k, bq, 64, fr, L, s, 70, causal)
+    else:
+        m = o.estimate_mask(q, k, bq, 64, tau, L, s, 70, causal)
+    np.testing.assert_array_equal(r["mask"]["levels"], m["levels"])
+    O, LSE = o.pyramid_attention(q, r["kpyr"], r["vpyr"], m["levels"], bq, 64, s, causal=causal)
+    np.testing.assert_array_equal(r["O"], O)
+    np.testing.assert_array_equal(r["LSE"], LSE)
+    # and attention over the unrounded pyramid differs (so the comparison above is not vacuous)
+    if io == "bf16":
+        kp_raw = [np.asarray(k, np.float64)] + o.build_pyramid(k, L)[1:]
+        vp_raw = [np.asarray(v, np.float64)] + o.build_pyramid(v, L)[1:]
+        O_raw, _ = o.pyramid_attention(q, kp_raw, vp_raw, m["levels"], bq, 64, s, causal=causal)
+        assert np.abs(O_raw - O).max() > 0
