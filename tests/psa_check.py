@@ -183,7 +183,7 @@ def check_attention(o_gpu: np.ndarray, o_ora: np.ndarray, label: str = "", rows=
 
 # ------------------------------------------------------------------------------ backward bounds
 
-BF16_HALF_ULP = 2.0 ** -9      # relative rounding error of a bf16 value (8 significant bits)
+BF16_UNIT = 2.0 ** -8          # largest relative rounding error of a bf16 value (8 significant bits)
 F32_UNIT = 2.0 ** -24          # relative rounding error of one float32 operation
 
 
@@ -192,8 +192,8 @@ def backward_bounds(q, k, v, L, level_map, q_block, scale, dO, dtype, causal=Fal
     gradients of psa_attention_bwd, derived from the roundings the kernels make.
 
     Per query row r and pooled key p (P = softmax weight, dP = <dO_r, V_p>, D = <dO_r, O_r>,
-    dA = P (dP - D), e = 2^-9 the relative error of a bf16 rounding, u = 2^-24 of a float32
-    operation):
+    dA = P (dP - D), e = 2^-8 the largest relative error of a bf16 rounding (8 significant
+    bits), u = 2^-24 of a float32 operation):
       * the forward's O carries |dO| <= e |O| (its bf16 rounding) + e sum_p P |V_p| (P is
         rounded to bf16 for the P.V product), so D is off by dD <= <|dO_r|, that bound>;
       * dP is a float32 sum of d exact bf16 products: ddP <= d u <|dO_r|, |V_p|>;
@@ -210,7 +210,7 @@ def backward_bounds(q, k, v, L, level_map, q_block, scale, dO, dtype, causal=Fal
     Returns a dict with bounds "dq", "dk", "dv" [like the gradients] and "dk_levels",
     "dv_levels" (per level, before the 1/c spread; float32 in the library's workspace)."""
     from oracle import psa_oracle as o
-    e, u = BF16_HALF_ULP, F32_UNIT
+    e, u = BF16_UNIT, F32_UNIT
     f32 = dtype == "f32"
     q = np.asarray(q, np.float64)
     dO = np.asarray(dO, np.float64)
@@ -277,7 +277,7 @@ def check_grad_bound(g, r, bound, label, out_dtype=None):
     element by element, with an absolute floor of 1e-6 of the largest reference entry.
     Returns the largest ratio of error to bound."""
     assert np.all(np.isfinite(g)), (label, "non-finite gradient")
-    tol = bound + (BF16_HALF_ULP * np.abs(r) if out_dtype == "bf16" else 0.0)
+    tol = bound + (BF16_UNIT * np.abs(r) if out_dtype == "bf16" else 0.0)
     tol = tol + 1e-6 * max(float(np.abs(r).max()), 1e-30)
     err = np.abs(g - r)
     bad = err > tol

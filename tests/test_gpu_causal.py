@@ -140,9 +140,9 @@ def test_causal_attention_arbitrary_maps(psa, case):
     B = rest[0] if rest else 1
     q, k, v = random_qkv(N + 17 + 1000 * (B - 1), B, H, H_kv, N, d, dtype)
     s = 1.0 / math.sqrt(d)
-    prob = psa.Problem(B=1, H=H, H_kv=H_kv, N=N, d=d, q_block=bq, num_levels=4, dtype=dtype, causal=True)
+    prob = psa.Problem(B=B, H=H, H_kv=H_kv, N=N, d=d, q_block=bq, num_levels=4, dtype=dtype, causal=True)
     rng = np.random.default_rng(N)
-    lev = rng.integers(-1, 4, size=(1, H, prob.nqb, prob.nkb)).astype(np.int8)
+    lev = rng.integers(-1, 4, size=(B, H, prob.nqb, prob.nkb)).astype(np.int8)
     lev[0, 0, 1] = 3                                  # a row whose first tiles are all in the future
     lev[0, 0, 1, :2] = -1
     say(f"{label}: causal attention on random level maps")
