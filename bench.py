@@ -7,9 +7,11 @@
 A step is one pass of the whole forward path over one batch of resident inputs:
 psa_build_pyramid, psa_estimate_mask (psa_estimate_mask_ranked with --rule ranked) and
 psa_attention_fwd, enqueued on one stream.
-W untimed steps, then K timed steps bracketed by device synchronisation; HIP events
-around every call give per-call times (the attention call is a single kernel launch,
-the roofline's kernel).
+W untimed steps, then K timed steps bracketed by device synchronisation (the "warm"
+loop: `value` and ms_per_step come from its wall clock); HIP events around every call
+give per-call times (the attention call is a single kernel launch, the roofline's
+kernel). Then K more steps, each after a 512 MiB write that evicts L2 and the MALL (the
+"cold" loop, outside `value`). Per call: mean, median, p10 and p90 of both loops.
 
 Throughput is effective TFLOP/s: FLOPs of QK^T and PV on the retained pooled rows
 only (sum over retained blocks of 4 * rows * pooled_rows * d), divided by the step
@@ -78,6 +80,19 @@ def effective_flops(level_map: np.ndarray, N: int, q_block: int, kv_block: int, 
     return 4.0 * d * total
 
 
+def tile_matrix_flops(level_map: np.ndarray, N: int, q_block: int, d: int) -> float:
+    """Matrix-core FLOPs the attention kernel executes: per query block, the tiles of its
+    level lists (2^l blocks of level l share one 64-key tile, so a level's last tile may be
+    part empty) times 64 keys x q_block query rows (a short last query block still runs whole
+    tiles) x 4d for QK^T and PV."""
+    lm = level_map.reshape(-1, level_map.shape[-1])
+    tiles = 0
+    for l in range(4):
+        cnt = (lm == l).sum(axis=1)
+        tiles += int(((cnt + (1 << l) - 1) >> l).sum())
+    return 4.0 * d * 64 * q_block * tiles
+
+
 def level_histogram(level_map: np.ndarray):
     return {str(l): int((level_map == l).sum()) for l in (-1, 0, 1, 2, 3)}
 
@@ -102,9 +117,11 @@ def traffic_from_profile():
 
 def cpu_baseline(w, q, k, v, tau, fractions=None):
     """Oracle (float64 NumPy) on a bounded sample: every step for about ten query heads (whole KV-head groups)."""
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import psa_oracle as o
 
+    cores = len(os.sched_getaffinity(0))        # the host cores this process may run on
+    threadpool_limits(cores)                    # the oracle's BLAS uses exactly those
     t0 = time.perf_counter()
     group = w.H // w.H_kv                       # query heads per KV head
     nkv = max(1, min(w.H_kv, 10 // group))      # whole groups, about ten query heads
@@ -117,7 +134,8 @@ def cpu_baseline(w, q, k, v, tau, fractions=None):
     dt = time.perf_counter() - t0
     fl = o.effective_flops(res["mask"]["levels"], w.N, w.q_block, w.kv_block, w.d, causal=w.causal)
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "blas_threads": int(threads),
+            "kind": "oracle",
             "sample": f"{w.name}: all three steps (pyramid, mask, attention) for heads 0..{nh - 1} of {w.H}, "
                       f"{fl:.3e} effective FLOPs in {dt:.1f} s, float64 NumPy"}
 
@@ -275,6 +293,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # warm: K steps back to back (the timed region of `value` and ms_per_step)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -285,6 +304,18 @@ def main():
     ms_step = wall * 1e3 / args.steps
     per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])   # ms
     pyr_ms, mask_ms, attn_ms = (float(np.mean(per[:, i])) for i in range(3))
+    # cold: K more steps, each after writing a 512 MiB buffer (evicts L2 and the 256 MB MALL,
+    # so the step's inputs come from HBM); the flush is outside the per-call events
+    print(f"[bench] cold loop ({args.steps} steps, 512 MiB flush before each)", file=sys.stderr, flush=True)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        flush.fill_(s & 0xFF)
+        step(cold_events[s])
+    torch.cuda.synchronize()
+    per_cold = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in cold_events])
+    del flush
 
     bwd = None
     if args.backward:
@@ -313,6 +344,16 @@ def main():
     mask_bytes = w.B * w.H * w.N * w.d * esz + k_bar.numel() * 4 + lm.size
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     traffic = traffic_from_profile()
+    tile_flops = tile_matrix_flops(lm, w.N, w.q_block, w.d)
+
+    def stats(x):
+        return {"mean": round(float(np.mean(x)), 4), "median": round(float(np.median(x)), 4),
+                "p10": round(float(np.percentile(x, 10)), 4), "p90": round(float(np.percentile(x, 90)), 4)}
+
+    calls = {}
+    for name, col in (("build_pyramid", 0), ("estimate_mask", 1), ("attention_fwd", 2)):
+        calls[name] = {"warm": stats(per[:, col]), "cold": stats(per_cold[:, col])}
+    step_cold = per_cold.sum(axis=1)
 
     result = {
         "metric": "PSA fwd ms/call + effective TFLOP/s (% MFMA peak) at 32760 tok, ~91% sparsity",
@@ -333,11 +374,25 @@ def main():
                      "traffic": traffic, "kernel": attention_kernel_name(w.d, w.q_block, w.dtype)},
         "calls_ms": {"build_pyramid": round(pyr_ms, 4), "estimate_mask": round(mask_ms, 4),
                      "attention_fwd": round(attn_ms, 4)},
+        "calls_ms_stats": calls,
+        "step_ms_cold": stats(step_cold),
+        "roofline_cold": {"achieved": round(flops / (float(np.median(per_cold[:, 2])) * 1e-3) / 1e12, 2),
+                          "frac": round(flops / (float(np.median(per_cold[:, 2])) * 1e-3) / 1e12
+                                        / PEAK_BF16_TFLOPS, 4),
+                          "of": "median attention_fwd duration of the cold loop"},
+        "tile_padding": {"matrix_flops": tile_flops, "effective_flops": flops,
+                         "padding_frac": round(1.0 - flops / tile_flops, 4) if tile_flops else None,
+                         "what": "matrix-core work the attention kernel's 64-key tiles and whole query "
+                                 "blocks execute (QK^T and PV), against the effective FLOPs"},
         "effective_flops": flops, "flop_fraction_rho": round(rho, 5),
         "hbm": {"build_pyramid_GBps": round(pyr_bytes / (pyr_ms * 1e-3) / 1e9, 1),
                 "build_pyramid_frac": round(pyr_bytes / (pyr_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "estimate_mask_GBps": round(mask_bytes / (mask_ms * 1e-3) / 1e9, 1),
                 "estimate_mask_frac": round(mask_bytes / (mask_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "build_pyramid_frac_cold": round(
+                    pyr_bytes / (float(np.median(per_cold[:, 0])) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "estimate_mask_frac_cold": round(
+                    mask_bytes / (float(np.median(per_cold[:, 1])) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "build_pyramid_bytes": pyr_bytes, "estimate_mask_bytes": mask_bytes},
         "levels": level_histogram(lm),
     }
