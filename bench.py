@@ -10,7 +10,7 @@ psa_attention_fwd, enqueued on one stream.
 W untimed steps, then K timed steps bracketed by device synchronisation (the "warm"
 loop: `value` and ms_per_step come from its wall clock); HIP events around every call
 give per-call times (the attention call is a single kernel launch, the roofline's
-kernel). Then K more steps, each after a 512 MiB write that evicts L2 and the MALL (the
+kernel). Then K more steps, each after a 512 MiB read that evicts L2 and the MALL (the
 "cold" loop, outside `value`). Per call: mean, median, p10 and p90 of both loops.
 
 Throughput is effective TFLOP/s: FLOPs of QK^T and PV on the retained pooled rows
@@ -304,14 +304,17 @@ def main():
     ms_step = wall * 1e3 / args.steps
     per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])   # ms
     pyr_ms, mask_ms, attn_ms = (float(np.mean(per[:, i])) for i in range(3))
-    # cold: K more steps, each after writing a 512 MiB buffer (evicts L2 and the 256 MB MALL,
-    # so the step's inputs come from HBM); the flush is outside the per-call events
-    print(f"[bench] cold loop ({args.steps} steps, 512 MiB flush before each)", file=sys.stderr, flush=True)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # cold: K more steps, each after reading a 512 MiB buffer (evicts L2 and the 256 MB MALL,
+    # so the step's inputs come from HBM). A read leaves only clean lines behind; a write
+    # would leave dirty ones whose write-back the next step would pay for. The flush is
+    # outside the per-call events.
+    print(f"[bench] cold loop ({args.steps} steps, 512 MiB read before each)", file=sys.stderr, flush=True)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     cold_events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
-        flush.fill_(s & 0xFF)
+        torch.sum(flush, dim=0, out=sink)
         step(cold_events[s])
     torch.cuda.synchronize()
     per_cold = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in cold_events])

@@ -19,7 +19,9 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpsa.so")
+# PSA_LIBRARY may name another build of the same C ABI (the sanitizer host check loads its
+# host-only build that way); by default the in-tree libpsa.so.
+LIB_PATH = os.environ.get("PSA_LIBRARY") or os.path.join(_HERE, "libpsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python level_pooled_kv_amd/build.py`")

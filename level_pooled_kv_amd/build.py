@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsa.so")
 
-SOURCES = ["psa_api.cpp", "psa_pyramid.hip", "psa_mask.hip", "psa_attention.hip", "psa_attention_bwd.hip"]
+SOURCES = ["psa_api.cpp", "psa_pyramid.hip", "psa_mask.hip", "psa_attention.hip", "psa_attention_bwd.hip",
+           "psa_noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -7,8 +7,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "psa_launch.h"
 
 namespace {
@@ -278,35 +276,6 @@ psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const f
                               stream, thresholds, nullptr, "psa_estimate_mask launch");
 }
 
-// Static workspace of psa_estimate_mask_noalloc: one copy per device, held until the
-// process ends. Host code never uses `scratch` itself (on the host the name is only a
-// stand-in for the symbol): each device's address comes from hipGetSymbolAddress, looked
-// up once per device with that device current, and only that address reaches a kernel.
-static __device__ __align__(256) unsigned char scratch[PSA_NOALLOC_SCRATCH_BYTES];
-
-namespace {
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch_ptr[kMaxDevices] = {};
-
-psa_status_t scratch_address(void** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(PSA_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_ptr[dev]) {
-    void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
-    if (!p) return fail(PSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
-    g_scratch_ptr[dev] = p;
-  }
-  *out = g_scratch_ptr[dev];
-  return PSA_OK;
-}
-}  // namespace
-
 psa_status_t psa_estimate_mask_noalloc(const psa_problem_t* prob, const void* q, const float* k_bar,
                                        const float* thresholds, int32_t n_dense_prefix, int8_t* level_map,
                                        float* cmass_out, hipStream_t stream) {
@@ -323,8 +292,8 @@ psa_status_t psa_estimate_mask_noalloc(const psa_problem_t* prob, const void* q,
                 "psa_estimate_mask_noalloc: the problem needs %zu bytes of workspace, the static scratch holds %zu",
                 need, (size_t)PSA_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
-  s = scratch_address(&ws);
-  if (s != PSA_OK) return s;
+  const hipError_t e = psa::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "psa_estimate_mask_noalloc: scratch lookup");
   return estimate_mask_common(prob, q, k_bar, n_dense_prefix, level_map, cmass_out, ws, PSA_NOALLOC_SCRATCH_BYTES,
                               stream, thresholds, nullptr, "psa_estimate_mask_noalloc launch");
 }

@@ -75,7 +75,15 @@ hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t stream);
 hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_similarity_cap(const CapArgs& a, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
-int mask_score_stride(int nkb);  // padded row length of the score workspace
+// Padded score-row length of the mask workspace: the smallest power of two >= max(nkb, 64).
+inline int mask_score_stride(int nkb) {
+  int n = 64;
+  while (n < nkb) n <<= 1;
+  return n;
+}
+// Device address of the static scratch of the allocation-free mask entry point on the
+// current device (looked up once per device); hipSuccess or the lookup's error.
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace psa

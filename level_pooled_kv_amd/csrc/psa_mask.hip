@@ -502,13 +502,6 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
   }
 }
 
-// Padded score-row length: the smallest power of two >= max(nkb, 64).
-int mask_score_stride(int nkb) {
-  int n = 64;
-  while (n < nkb) n <<= 1;
-  return n;
-}
-
 template <int E, bool RANKED>
 static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
   RankFractions frac;
