@@ -51,7 +51,7 @@ namespace psa {
 // merged through LDS at the end. This keeps four waves per workgroup, hence two per
 // SIMD, where two-wave workgroups would leave one (the LDS holds two per CU).
 template <typename T, int D, int NW, int KS>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2)))
 pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                         const T* __restrict__ kp, const T* __restrict__ vp,
                         const int8_t* __restrict__ level_map, T* __restrict__ o, float* __restrict__ lse,
@@ -69,7 +69,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   __shared__ __align__(16) uint16_t V0[64 * D], V1[64 * D];
   __shared__ float corr[2][64];
   __shared__ int ltok[2][64];                    // diagonal tiles: last token of each staged key row
-  __shared__ int16_t blist[kMaxKvBlocks];
+  __shared__ __align__(16) int16_t blist[kMaxKvBlocks + 8];  // + 8: a tile's segment lookups stay in the array
   __shared__ uint32_t tdesc[kMaxKvBlocks + 4];   // per tile: level | list base << 2 | segs << 16 | irregular << 31
   __shared__ int s_tile[5];
 
@@ -180,7 +180,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       const int row = st_row0 + RPB * i;
       const int seg = row >> sh;
       const bool vseg = seg < ti.nseg;
-      const int blk = vseg ? (int)blist[ti.base + seg] : 0;
+      const int blk = (int)blist[ti.base + seg];     // unused (row not ok) past the valid segments
       const int prow = blk * seglen + (row & (seglen - 1));
       const bool ok = vseg && prow < rows_lv;
       const int rowel = (ok ? prow : 0) * D;
@@ -221,7 +221,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       const int row = st_row0 + RPB * i;
       const int seg = row >> sh;
       const bool vseg = seg < ti.nseg;
-      const int blk = vseg ? (int)blist[ti.base + seg] : 0;
+      const int blk = (int)blist[ti.base + seg];     // unused (row not ok) past the valid segments
       const int prow = blk * seglen + (row & (seglen - 1));
       const bool ok = vseg && prow < rows_lv;
       const int rowel = (ok ? prow : 0) * D;
@@ -403,9 +403,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     // merge the two key halves' softmax states of each query: the khalf = 1 waves hand
     // (max, partial sums, O^T) to the khalf = 0 waves of the same rows through LDS (the
     // tile buffers are idle: the loop's last barrier follows its last loads)
+    static_assert(RW <= 4, "one tile buffer per row group");
     const int rw = wave % RW;
-    float* xo = reinterpret_cast<float*>(rw == 0 ? K0 : K1);   // [tt][x][lane]
-    float* xs = reinterpret_cast<float*>(V0) + rw * 128;        // [m, l][lane]
+    float* xo = reinterpret_cast<float*>(rw == 0 ? K0 : rw == 1 ? K1 : rw == 2 ? V0 : V1);   // [tt][x][lane]
+    float* xs = reinterpret_cast<float*>(blist) + rw * 128;     // [m, l][lane]
     if (khalf == 1) {
 #pragma unroll
       for (int tt = 0; tt < C::kDt; ++tt)

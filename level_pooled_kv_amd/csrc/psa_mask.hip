@@ -8,21 +8,26 @@
 // into a probability mass, rank blocks by score (ties by index), and give block j
 // the lowest level l whose threshold exceeds the mass ranked strictly ahead of j.
 //
-// Three kernels:
+// Kernels:
 //  * qblock_mean_kernel streams Q once (HBM-bound: every load of a thread is in
-//    flight at once, 16-byte loads, whole rows per wave) and writes the float32
-//    mean query of each query block to the workspace.
+//    flight at once, 16-byte loads, whole rows per wave, two query blocks per
+//    workgroup) and writes the float32 mean query of each query block to the workspace.
 //  * block_score_kernel: z = scale * qbar kbar^T + ln n_j per head on the float32
 //    matrix cores (v_mfma_f32_32x32x2_f32), one 32 x 32 tile per wave, into a
 //    workspace row of n_pad floats per query block.
+//  * qblock_score_kernel (rows of more than 512 KV blocks): both of the above in one
+//    pass, the mean queries kept in LDS, 16 x 16 score tiles per product.
 //  * block_level_kernel: one wave per query-block row: softmax of the row, a
 //    bitonic sort of score keys held in registers (n_pad / 64 per lane; partners
 //    in other lanes come through cross-lane shuffles, so no LDS and no workgroup
 //    barrier), a wave-wide exclusive scan of the masses in rank order, the
 //    threshold compares and the int8 level writes. 32-bit keys settle a row unless
 //    a cut splits a group of equal scores; such rows, and calls that want the
-//    cumulative mass, sort 64-bit (score, index) keys (for rows of more than 512
-//    blocks in a second kernel over the rows the first one flags).
+//    cumulative mass, sort 64-bit (score, index) keys.
+//  * block_level_cand_kernel (rows of more than 512 KV blocks, no cumulative mass
+//    asked): a score cut found by bisection leaves out only blocks that take no level,
+//    and only the candidates above it are sorted; rows it cannot settle are flagged for
+//    block_level_kernel's exact pass.
 //    Its ranked form (the quantile rule the top168.com ablation compares with
 //    thresholds; fixed shares of the score-ranked blocks per level: skillmd.com,
 //    "Level assignment") gives the block at rank r the lowest level l with
@@ -35,47 +40,55 @@ namespace psa {
 
 constexpr int kMaskThreads = 256;
 
-template <typename T, int D>
+template <typename T, int D, int QB>
 __global__ void __launch_bounds__(kMaskThreads)
 qblock_mean_kernel(const T* __restrict__ q, float* __restrict__ qbar, int N, int q_block, int nqb) {
   constexpr int E = io_traits<T>::per16;
   constexpr int CPR = D / E;                // 16-byte chunks per row
   constexpr int G = kMaskThreads / CPR;     // row groups
   constexpr int MAXR = 128 / G;             // rows per thread at the largest query block
-  __shared__ float red[G][D];
+  __shared__ float red[QB][G][D];
   const int t = threadIdx.x;
   const int chunk = t % CPR, g = t / CPR;
-  const int i = blockIdx.x;
   const int64_t bh = blockIdx.y;
-  const int r0 = i * q_block;
-  const int m = min(q_block, N - r0);
-  const T* src = q + (bh * N + r0) * (int64_t)D + chunk * E;
+  const int i0 = blockIdx.x * QB;           // QB query blocks per workgroup: every load in flight at once
 
-  // rows g, g+G, g+2G, ...: all loads issued before any is used
-  U128 raw[MAXR];
+  U128 raw[QB][MAXR];
 #pragma unroll
-  for (int r = 0; r < MAXR; ++r) {
-    const int row = g + r * G;
-    raw[r] = row < m ? ld128(src + (int64_t)row * D) : U128{{0u, 0u, 0u, 0u}};
-  }
-  float acc[E];
+  for (int u = 0; u < QB; ++u) {
+    const int r0 = (i0 + u) * q_block;
+    const int m = i0 + u < nqb ? min(q_block, N - r0) : 0;
+    const T* src = q + (bh * N + r0) * (int64_t)D + chunk * E;
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int r = 0; r < MAXR; ++r) {
-    float x[E];
-    unpack16<T>(raw[r], x);
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += x[e];
+    for (int r = 0; r < MAXR; ++r) {
+      const int row = g + r * G;
+      raw[u][r] = row < m ? ld128(src + (int64_t)row * D) : U128{{0u, 0u, 0u, 0u}};
+    }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) red[g][chunk * E + e] = acc[e];
+  for (int u = 0; u < QB; ++u) {
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      float x[E];
+      unpack16<T>(raw[u][r], x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[u][g][chunk * E + e] = acc[e];
+  }
   __syncthreads();
-  if (t < D) {
+  for (int x = t; x < QB * D; x += kMaskThreads) {
+    const int u = x / D, c = x - u * D;
+    const int i = i0 + u;
+    if (i >= nqb) continue;
     float s = 0.f;
 #pragma unroll 8
-    for (int gg = 0; gg < G; ++gg) s += red[gg][t];
-    qbar[(bh * nqb + i) * D + t] = s / (float)m;
+    for (int gg = 0; gg < G; ++gg) s += red[u][gg][c];
+    qbar[(bh * nqb + i) * D + c] = s / (float)min(q_block, N - i * q_block);
   }
 }
 
@@ -162,6 +175,122 @@ block_score_kernel(const float* __restrict__ qbar, const float* __restrict__ kba
       for (int x = 0; x < 4; ++x)
         if (j0 + x < nkb) zr[j0 + x] = out[x];
     }
+  }
+}
+
+// For rows of more than 512 KV blocks, where the score products dominate: query-block means
+// and block scores in one pass, one workgroup per (b, h) and 16 consecutive query blocks.
+// The workgroup streams the 16 blocks' rows of Q once (the next block's loads in flight
+// while the current one is reduced), keeps the float32 mean queries in LDS (the B operand)
+// and computes z = scale * qbar kbar^T + ln n_j on the float32 matrix cores
+// (v_mfma_f32_16x16x4_f32: 16 KV blocks x 16 query blocks per product), k_bar coming
+// straight from global memory as the A operand, so neither the mean queries nor a k_bar
+// tile pass through LDS staging. Two tiles per step give each wave two independent
+// product chains.
+template <typename T, int D>
+__global__ void __launch_bounds__(kMaskThreads)
+qblock_score_kernel(const T* __restrict__ q, const float* __restrict__ kbar, float* __restrict__ z, int N,
+                    int H, int H_kv, int q_block, int nqb, int nkb, int zstride, float scale) {
+  constexpr int R = 16;                     // query blocks per workgroup (the 16 product columns)
+  constexpr int E16 = io_traits<T>::per16;  // elements per 16-byte chunk
+  constexpr int CPR = D / E16;              // chunks per row
+  constexpr int G = kMaskThreads / CPR;     // row groups
+  constexpr int MAXR = 128 / G;             // rows per thread per query block (q_block <= 128)
+  constexpr int QS = D + 4;                 // padded LDS row of the mean queries (floats)
+  __shared__ __align__(16) float qs[R * QS];
+  __shared__ float red[G][D];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int i0 = blockIdx.x * R;            // first query block of the workgroup
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int g = h / (H / H_kv);
+  const int nrow = min(R, nqb - i0);        // query blocks present
+  const int chunk = t % CPR, grp = t / CPR;
+  const T* qh = q + (int64_t)bh * N * D + chunk * E16;
+
+  for (int x = t; x < R * QS; x += kMaskThreads)   // absent query blocks: zero columns
+    if (x / QS >= nrow) qs[x] = 0.f;
+
+  auto load_block = [&](int r, U128 (&raw)[MAXR]) {
+    const int r0 = (i0 + r) * q_block;
+    const int m = r < nrow ? min(q_block, N - r0) : 0;
+#pragma unroll
+    for (int k = 0; k < MAXR; ++k) {
+      const int row = grp + k * G;
+      raw[k] = row < m ? ld128(qh + (int64_t)(r0 + row) * D) : U128{{0u, 0u, 0u, 0u}};
+    }
+  };
+  U128 buf[2][MAXR];
+  load_block(0, buf[0]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r + 1 < R) load_block(r + 1, buf[(r + 1) & 1]);
+    float acc[E16];
+#pragma unroll
+    for (int e = 0; e < E16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXR; ++k) {
+      float x[E16];
+      unpack16<T>(buf[r & 1][k], x);
+#pragma unroll
+      for (int e = 0; e < E16; ++e) acc[e] += x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E16; ++e) red[grp][chunk * E16 + e] = acc[e];
+    __syncthreads();
+    if (t < D && r < nrow) {
+      float sum = 0.f;
+#pragma unroll 8
+      for (int gg = 0; gg < G; ++gg) sum += red[gg][t];
+      qs[r * QS + t] = sum / (float)min(q_block, N - (i0 + r) * q_block);
+    }
+    __syncthreads();
+  }
+
+  // scores: wave w takes 16-block tiles w + 8u and w + 8u + 4. Lane l supplies KV block
+  // 16 tile + l%16 (operand A) and query column l%16 (operand B) at d = 16c + 4(l/16) + 0..3
+  // (one float4 of each feeds four products), and receives blocks 16 tile + 4(l/16) + 0..3
+  // of query column l%16.
+  const float* kb = kbar + (int64_t)(b * H_kv + g) * nkb * D;
+  const int ntiles = (nkb + 15) / 16;
+  const int n = lane & 15, kq = lane >> 4;
+  const float* qcol = qs + n * QS + 4 * kq;
+  float* zr = z + ((int64_t)bh * nqb + i0 + n) * zstride;
+  auto store = [&](int tile, const f32x4& acc) {
+    if (n >= nrow || tile >= ntiles) return;
+    const int j0 = tile * 16 + 4 * kq;
+    float out[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) out[x] = fmaf(scale, acc[x], logf((float)min(64, N - 64 * (j0 + x))));
+    if (j0 + 3 < nkb) {
+      *reinterpret_cast<float4*>(zr + j0) = make_float4(out[0], out[1], out[2], out[3]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        if (j0 + x < nkb) zr[j0 + x] = out[x];
+    }
+  };
+  for (int tile = wave; tile < ntiles; tile += 2 * (kMaskThreads / 64)) {
+    const int tile1 = tile + kMaskThreads / 64;
+    const float* krow0 = kb + (int64_t)min(tile * 16 + n, nkb - 1) * D + 4 * kq;
+    const float* krow1 = kb + (int64_t)min(tile1 * 16 + n, nkb - 1) * D + 4 * kq;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const float4 a0 = *reinterpret_cast<const float4*>(krow0 + 16 * c);
+      const float4 a1 = *reinterpret_cast<const float4*>(krow1 + 16 * c);
+      const float4 bq = *reinterpret_cast<const float4*>(qcol + 16 * c);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.x, bq.x, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.x, bq.x, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.y, bq.y, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.y, bq.y, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.z, bq.z, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.z, bq.z, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.w, bq.w, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.w, bq.w, acc1, 0, 0, 0);
+    }
+    store(tile, acc0);
+    store(tile1, acc1);
   }
 }
 
@@ -309,10 +438,10 @@ __device__ __forceinline__ float wave_exclusive_sum(float tot, int lane) {
 // orders by block index). Exact path, for such rows and for calls that want the
 // cumulative mass itself: sort 64-bit (score, index) keys. Both paths sum the same
 // masses in the same order, so they give the same levels. MODE 0 runs both in one
-// kernel (the exact path only for rows the fast one cannot settle); for long rows the
-// two are separate kernels, which keeps the fast one small enough for several waves
-// per SIMD: MODE 1 is the fast path, flagging such rows in need_exact, MODE 2 the exact
-// path over the flagged rows (every row when need_exact is null).
+// kernel (the exact path only for rows the fast one cannot settle); MODE 1 is the fast
+// path alone, flagging such rows in need_exact, MODE 2 the exact path over the flagged
+// rows (every row when need_exact is null). Rows of more than 512 blocks take
+// block_level_cand_kernel as their fast pass and MODE 2 after it.
 template <int E, bool RANKED, int MODE>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
@@ -502,6 +631,207 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
   }
 }
 
+// Fast pass for long rows (more than 512 KV blocks), in place of the sort of the whole
+// padded row: a block ranked behind blocks holding at least tau_{L-1} of the mass (the
+// ranked rule: at least K_{L-1} blocks) can take no level, so a score cut x with
+// M(z > x) >= tau_{L-1} (plus a margin far above the float32 error of that sum) leaves out
+// only pruned blocks. Bisection on x finds one that keeps at most half the padded row
+// (32 E candidates); the candidates' 32-bit keys are compacted into LDS (wave-private) and
+// sorted, and the cuts come from their prefix masses exactly as in block_level_kernel's
+// fast path (the blocks ahead of a candidate are all candidates, so its mass ranked ahead
+// is complete). Rows where no such cut exists, or where a cut splits equal scores, are
+// flagged in need_exact for the exact pass. The row max and mass sum are taken in the
+// same grouping as block_level_kernel's (E consecutive blocks per lane), so every block's
+// mass is the same float.
+template <int E, bool RANKED>
+__global__ void __launch_bounds__(kMaskThreads)
+block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map,
+                        uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
+                        float tau0, float tau1, float tau2, float tau3, RankFractions frac, int q_block, int nqb,
+                        int causal) {
+  constexpr int NP = 64 * E;
+  constexpr int EC = E / 2;                 // candidate keys per lane in the sort
+  constexpr int kCand = 64 * EC;
+  __shared__ __align__(16) uint32_t cbuf[kMaskThreads / 64][kCand];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * (kMaskThreads / 64) + wave;
+  if (row >= nrows) return;                 // whole wave; wave-private LDS, no barrier
+  int nvis = nkb, dfirst = nkb;
+  if (causal) {
+    const int r0 = (row % nqb) * q_block;
+    nvis = (min(N, r0 + q_block) - 1) / 64 + 1;
+    dfirst = r0 / 64;
+  }
+  const float* zr = z + (int64_t)row * NP + E * lane;
+  float zz[E];
+#pragma unroll
+  for (int c = 0; c < E / 4; ++c) {   // the row's scores only, not its padding (groups of 4 stay in the row)
+    const float4 f = E * lane + 4 * c < nkb ? reinterpret_cast<const float4*>(zr)[c]
+                                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    zz[4 * c] = f.x; zz[4 * c + 1] = f.y; zz[4 * c + 2] = f.z; zz[4 * c + 3] = f.w;
+  }
+  int8_t* lrow = level_map + (int64_t)row * nkb;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int j = E * lane + r;
+    if (j < nvis) mx = fmaxf(mx, zz[r]);
+    else {
+      if (j < nkb) lrow[j] = -1;            // causal: blocks after the query block
+      zz[r] = -INFINITY;                    // never a candidate
+    }
+  }
+  mx = wave_max(mx);
+  float ez[E], s = 0.f;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    ez[r] = E * lane + r < nvis ? __expf(zz[r] - mx) : 0.f;
+    s += ez[r];
+  }
+  s = wave_sum(s);
+  const float inv_s = 1.0f / s;
+  const float tau[4] = {tau0, tau1, tau2, tau3};
+  int K[4];
+#pragma unroll
+  for (int l = 0; l < 4; ++l) K[l] = RANKED && l < L ? (int)floor(frac.f[l] * (double)nvis) : 0;
+
+  // ---- the score cut: every visible block when they fit, else bisection
+  bool fail = false;
+  float x = -INFINITY;
+  if (nvis > kCand) {
+    const float T = tau[L - 1] + 2e-6f;     // mass that must lie above the cut (threshold rule)
+    const int Kt = K[L - 1];                // blocks that must lie above the cut (ranked rule)
+    fail = RANKED ? Kt > kCand : T > 0.999f;
+    float zmin = INFINITY;
+#pragma unroll
+    for (int r = 0; r < E; ++r)
+      if (E * lane + r < nvis) zmin = fminf(zmin, zz[r]);
+    zmin = -wave_max(-zmin);
+    float lo = zmin - 1.0f, hi = mx;        // lo: a valid cut (every visible block above it)
+    bool found = false;
+    for (int it = 0; it < 40 && !fail && !found; ++it) {
+      const float mid = 0.5f * (lo + hi);
+      if (!(mid > lo && mid < hi)) break;   // float resolution exhausted
+      float m = 0.f;
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const bool above = zz[r] > mid;
+        m += above ? ez[r] : 0.f;
+        cnt += __popcll(__ballot(above));
+      }
+      const bool ok = RANKED ? cnt >= Kt : wave_sum(m) * inv_s >= T;
+      if (ok) {
+        lo = mid;
+        found = cnt <= kCand;
+      } else {
+        hi = mid;
+      }
+    }
+    fail = fail || !found;
+    x = lo;
+  }
+
+  // ---- compact the candidates' keys (order within the buffer does not matter: sorted next)
+  uint32_t key[EC];
+  int ncand = 0;
+  uint32_t* buf = cbuf[wave];
+  if (!fail) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const bool cand = zz[r] > x;          // invisible blocks hold -inf
+      const uint64_t m = __ballot(cand);
+      const int pos = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      if (cand) buf[pos] = score_key(zz[r]);
+      ncand += __popcll(m);
+    }
+#pragma unroll
+    for (int c = 0; c < EC; ++c)
+      if (lane + 64 * c >= ncand) buf[lane + 64 * c] = kPadKey32;
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < EC / 4; ++c) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(buf + EC * lane + 4 * c);
+      key[4 * c] = kk.x; key[4 * c + 1] = kk.y; key[4 * c + 2] = kk.z; key[4 * c + 3] = kk.w;
+    }
+    wave_bitonic_sort32<EC>(key, lane);
+  }
+
+  if (!fail) {
+    bool tie = false;
+#pragma unroll
+    for (int r = 0; r + 1 < EC; ++r) tie |= key[r] == key[r + 1] && key[r] != kPadKey32;
+    const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
+    tie |= lane < 63 && key[EC - 1] == next_first && key[EC - 1] != kPadKey32;
+    const bool any_tie = __ballot(tie) != 0;
+    int cnt[kMaxLevels] = {0, 0, 0, 0};
+    if constexpr (RANKED) {
+#pragma unroll
+      for (int l = 0; l < kMaxLevels; ++l) cnt[l] = K[l];
+    } else {
+      float p[EC], tot = 0.f;
+#pragma unroll
+      for (int r = 0; r < EC; ++r) {
+        p[r] = key[r] != kPadKey32 ? __expf(key32_score(key[r]) - mx) * inv_s : 0.f;
+        tot += p[r];
+      }
+      float run = wave_exclusive_sum(tot, lane);
+      int lc[kMaxLevels] = {0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < EC; ++r) {
+        const float C = run;
+        run += p[r];
+        const bool real = key[r] != kPadKey32;
+#pragma unroll
+        for (int l = 0; l < kMaxLevels; ++l) lc[l] += real && C < tau[l] ? 1 : 0;
+      }
+#pragma unroll
+      for (int l = 0; l < kMaxLevels; ++l) cnt[l] = (int)wave_sum((float)lc[l]);   // exact: counts < 2^24
+    }
+    uint32_t cut[kMaxLevels];
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) {
+      const int pos = cnt[l] - 1;
+      uint32_t v = key[0];
+#pragma unroll
+      for (int r = 1; r < EC; ++r)
+        if (pos >= 0 && pos % EC == r) v = key[r];
+      cut[l] = pos >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v, pos / EC) : 0u;
+    }
+    if (any_tie) {
+      int le[kMaxLevels] = {0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const bool vis = E * lane + r < nvis;
+        const uint32_t kr = score_key(zz[r]);
+#pragma unroll
+        for (int l = 0; l < kMaxLevels; ++l) le[l] += vis && kr <= cut[l] ? 1 : 0;
+      }
+#pragma unroll
+      for (int l = 0; l < kMaxLevels; ++l)
+        if (l < L && cnt[l] > 0) fail |= (int)wave_sum((float)le[l]) > cnt[l];   // exact: counts < 2^24
+    }
+    if (!fail) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const int j = E * lane + r;
+        if (j < nvis) {
+          const uint32_t kr = score_key(zz[r]);
+          int lev = -1;
+#pragma unroll
+          for (int l = kMaxLevels - 1; l >= 0; --l)
+            if (l < L && cnt[l] > 0 && kr <= cut[l]) lev = l;
+          if (64 * j < n_dense_prefix || j >= dfirst) lev = 0;
+          lrow[j] = (int8_t)lev;
+        }
+      }
+    }
+  }
+  if (lane == 0) need_exact[row] = fail ? 1 : 0;
+}
+
 template <int E, bool RANKED>
 static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
   RankFractions frac;
@@ -515,9 +845,9 @@ static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
   } else {
     // without cmass: the fast pass, then the exact pass over the rows it flagged
     if (a.cmass == nullptr)
-      hipLaunchKernelGGL((block_level_kernel<E, RANKED, 1>), grid, dim3(kMaskThreads), 0, stream, a.z,
-                         a.level_map, a.cmass, a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0],
-                         a.tau[1], a.tau[2], a.tau[3], frac, a.q_block, a.nqb, causal);
+      hipLaunchKernelGGL((block_level_cand_kernel<E, RANKED>), grid, dim3(kMaskThreads), 0, stream, a.z,
+                         a.level_map, a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0], a.tau[1],
+                         a.tau[2], a.tau[3], frac, a.q_block, a.nqb, causal);
     hipLaunchKernelGGL((block_level_kernel<E, RANKED, 2>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
                        a.cmass, a.cmass == nullptr ? a.need_exact : nullptr, a.N, a.nkb, nrows, a.L,
                        a.n_dense_prefix, a.tau[0], a.tau[1], a.tau[2], a.tau[3], frac, a.q_block, a.nqb, causal);
@@ -532,15 +862,23 @@ static void launch_level_e(const MaskArgs& a, int nrows, hipStream_t stream) {
 
 template <typename T, int D>
 static hipError_t launch_mask_t(const MaskArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((qblock_mean_kernel<T, D>), dim3(a.nqb, a.B * a.H), dim3(kMaskThreads), 0, stream,
-                     static_cast<const T*>(a.q), a.qbar, a.N, a.q_block, a.nqb);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int zstride = mask_score_stride(a.nkb);
-  const int ktiles = (a.nkb + 31) / 32;
-  dim3 sgrid((ktiles + kScoreWaves - 1) / kScoreWaves, (a.nqb + 31) / 32, a.B * a.H);
-  hipLaunchKernelGGL((block_score_kernel<D>), sgrid, dim3(64 * kScoreWaves), 0, stream, a.qbar, a.k_bar, a.z, a.N,
-                     a.H, a.H_kv, a.nqb, a.nkb, zstride, a.scale);
+  hipError_t e;
+  if (a.nkb > 512) {
+    hipLaunchKernelGGL((qblock_score_kernel<T, D>), dim3((a.nqb + 15) / 16, a.B * a.H), dim3(kMaskThreads), 0,
+                       stream, static_cast<const T*>(a.q), a.k_bar, a.z, a.N, a.H, a.H_kv, a.q_block, a.nqb, a.nkb,
+                       zstride, a.scale);
+  } else {
+    constexpr int QB = 2;
+    hipLaunchKernelGGL((qblock_mean_kernel<T, D, QB>), dim3((a.nqb + QB - 1) / QB, a.B * a.H), dim3(kMaskThreads),
+                       0, stream, static_cast<const T*>(a.q), a.qbar, a.N, a.q_block, a.nqb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int ktiles = (a.nkb + 31) / 32;
+    dim3 sgrid((ktiles + kScoreWaves - 1) / kScoreWaves, (a.nqb + 31) / 32, a.B * a.H);
+    hipLaunchKernelGGL((block_score_kernel<D>), sgrid, dim3(64 * kScoreWaves), 0, stream, a.qbar, a.k_bar, a.z,
+                       a.N, a.H, a.H_kv, a.nqb, a.nkb, zstride, a.scale);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrows = a.B * a.H * a.nqb;

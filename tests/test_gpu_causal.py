@@ -15,7 +15,7 @@ import torch
 from oracle import psa_oracle as o
 from synth import generate, get as get_workload, random_qkv
 from tests.oracle_heads import compare_heads
-from tests.psa_check import (check_attention, check_cmass, check_kbar, check_mask, check_mask_ranked,
+from tests.psa_check import (check_attention, check_cmass, check_fast_vs_exact, check_kbar, check_mask, check_mask_ranked,
                               lse_tolerance, to_device, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -187,9 +187,12 @@ def test_causal_mask_long_rows(psa, ranked):
         lev_c, _ = psa.psa_estimate_mask_ranked(prob, qd, kbar, fr, want_cmass=True)
     else:
         lev, _ = psa.psa_estimate_mask(prob, qd, kbar, tau)
-        lev_c, _ = psa.psa_estimate_mask(prob, qd, kbar, tau, want_cmass=True)
+        lev_c, cm_c = psa.psa_estimate_mask(prob, qd, kbar, tau, want_cmass=True)
     torch.cuda.synchronize()
-    assert torch.equal(lev, lev_c)
+    if ranked:
+        assert torch.equal(lev, lev_c)       # ranks involve no mass sums: both passes agree exactly
+    else:
+        check_fast_vs_exact(lev.cpu().numpy(), lev_c.cpu().numpy(), to_host(cm_c), tau, L, label="causal long rows")
     lev_g = lev.cpu().numpy()
     vis, diag = o.causal_blocks(N, 128, 64)
     assert np.all(lev_g[..., ~vis] == -1) and np.all(lev_g[..., diag] == 0)
@@ -204,6 +207,7 @@ def test_causal_mask_long_rows(psa, ranked):
     else:
         m = o.estimate_mask(q, k, 128, 64, tau, L, s, causal=True)
         check_mask(lev_g, m, tau, L, 0, label="causal, long rows")
+        check_mask(lev_c.cpu().numpy(), m, tau, L, 0, label="causal, long rows, exact pass")
     say("causal mask, long rows: ok")
 
 
