@@ -97,10 +97,11 @@ def level_histogram(level_map: np.ndarray):
     return {str(l): int((level_map == l).sum()) for l in (-1, 0, 1, 2, 3)}
 
 
-def traffic_from_profile():
+def traffic_from_profile(workload: str, plain_step: bool):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
-    was taken on the current attention source (else None)."""
-    if not os.path.exists(TRAFFIC_FILE):
+    was taken on the current attention source and on this workload's default step (else
+    None)."""
+    if workload != "wan13b" or not plain_step or not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
@@ -346,7 +347,7 @@ def main():
     pyr_bytes = kv_bytes + 2 * w.B * w.H_kv * R * w.d * esz + k_bar.numel() * 4
     mask_bytes = w.B * w.H * w.N * w.d * esz + k_bar.numel() * 4 + lm.size
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile(w.name, fractions is None and args.similarity is None)
     tile_flops = tile_matrix_flops(lm, w.N, w.q_block, w.d)
 
     def stats(x):
