@@ -38,11 +38,12 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan13b_traffic.txt")
 ATTN_SOURCES = [os.path.join(ROOT, "level_pooled_kv_amd", "csrc", f)
                 for f in ("psa_attn_common.h", "psa_attention.hip")]
+MASK_SOURCES = [os.path.join(ROOT, "level_pooled_kv_amd", "csrc", "psa_mask.hip")]
 
 
-def attention_source_hash() -> str:
+def attention_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in sources or ATTN_SOURCES:
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
@@ -97,10 +98,11 @@ def level_histogram(level_map: np.ndarray):
     return {str(l): int((level_map == l).sum()) for l in (-1, 0, 1, 2, 3)}
 
 
-def traffic_from_profile(workload: str, plain_step: bool):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
-    was taken on the current attention source and on this workload's default step (else
-    None)."""
+def traffic_from_profile(workload: str, plain_step: bool, key: str = "hbm_bytes_per_launch",
+                         hash_key: str = "attention_source_sha256", sources=None):
+    """HBM bytes from the committed rocprofv3 counter summary (per attention launch by
+    default; key selects another figure), if it was taken on the current source of those
+    kernels and on this workload's default step (else None)."""
     if workload != "wan13b" or not plain_step or not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -108,10 +110,10 @@ def traffic_from_profile(workload: str, plain_step: bool):
         if "=" in line and not line.lstrip().startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("attention_source_sha256") != attention_source_hash():
+    if kv.get(hash_key) != attention_source_hash(sources or ATTN_SOURCES):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -348,6 +350,9 @@ def main():
     mask_bytes = w.B * w.H * w.N * w.d * esz + k_bar.numel() * 4 + lm.size
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name, fractions is None and args.similarity is None)
+    # measured bytes of the mask kernels, their float32 scratch (query means, score rows) included
+    mask_traffic = traffic_from_profile(w.name, fractions is None and args.similarity is None,
+                                        "mask_hbm_bytes_per_call", "mask_source_sha256", MASK_SOURCES)
     tile_flops = tile_matrix_flops(lm, w.N, w.q_block, w.d)
 
     def stats(x):
@@ -397,7 +402,8 @@ def main():
                     pyr_bytes / (float(np.median(per_cold[:, 0])) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 "estimate_mask_frac_cold": round(
                     mask_bytes / (float(np.median(per_cold[:, 1])) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "build_pyramid_bytes": pyr_bytes, "estimate_mask_bytes": mask_bytes},
+                "build_pyramid_bytes": pyr_bytes, "estimate_mask_bytes": mask_bytes,
+                "estimate_mask_traffic_bytes": mask_traffic},
         "levels": level_histogram(lm),
     }
     if bwd is not None:

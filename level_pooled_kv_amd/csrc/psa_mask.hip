@@ -36,6 +36,8 @@
 #include "psa_device.h"
 #include "psa_launch.h"
 
+#include <cmath>
+
 namespace psa {
 
 constexpr int kMaskThreads = 256;
@@ -420,33 +422,40 @@ __device__ __forceinline__ void wave_bitonic_sort32(uint32_t (&key)[E], int lane
   }
 }
 
-// Exclusive prefix, across the wave, of per-lane totals.
-__device__ __forceinline__ float wave_exclusive_sum(float tot, int lane) {
-  float incl = tot;
+// Block masses in fixed point: p * 2^31 rounded to an integer (p <= 1, and the masses of
+// a row add up to about 2^31, so every partial sum fits 32 bits). Integer sums do not
+// depend on the order of the additions, so every pass (sorted scan, bucket histogram)
+// finds the same mass ranked ahead of a block, and C * 2^-31 < tau holds exactly when
+// C < ceil(tau * 2^31) (the host's mass_threshold).
+constexpr float kMassScale = 2147483648.0f;
+__device__ __forceinline__ uint32_t mass_units(float p) { return __float2uint_rn(p * kMassScale); }
+
+// Exclusive prefix, across the wave, of per-lane totals (exact).
+__device__ __forceinline__ uint32_t wave_exclusive_sum_u32(uint32_t tot, int lane) {
+  uint32_t incl = tot;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(incl, o);
+    const uint32_t y = (uint32_t)__shfl_up((int)incl, o);
     if (lane >= o) incl += y;
   }
   return incl - tot;
 }
 
-// One wave per query-block row. Fast path (no cmass): sort the 32-bit score keys; the
-// mass ranked ahead of a block is a prefix of the sorted masses, so level l takes the
-// blocks whose key is at most the key at the last sorted position with prefix mass
-// below tau_l, unless that key continues past the cut (equal scores, which the rule
-// orders by block index). Exact path, for such rows and for calls that want the
-// cumulative mass itself: sort 64-bit (score, index) keys. Both paths sum the same
-// masses in the same order, so they give the same levels. MODE 0 runs both in one
-// kernel (the exact path only for rows the fast one cannot settle); MODE 1 is the fast
-// path alone, flagging such rows in need_exact, MODE 2 the exact path over the flagged
-// rows (every row when need_exact is null). Rows of more than 512 blocks take
-// block_level_cand_kernel as their fast pass and MODE 2 after it.
+// One wave per query-block row. Exact path: sort 64-bit (score, index) keys, scan the
+// integer masses in rank order and compare them with the thresholds (the ranked rule:
+// compare the sorted position with K_l), writing the cumulative mass when asked. MODE 2
+// runs it over the rows flagged in need_exact (every row when need_exact is null), after
+// a fast pass: block_level_sel_kernel for the threshold rule, block_level_cand_kernel for
+// the ranked rule on rows of more than 512 blocks. MODE 0 (ranked rule, shorter rows)
+// first tries the fast path in this kernel: sort the 32-bit score keys; level l takes the
+// blocks whose key is at most the key at sorted position K_l - 1, unless that key
+// continues past the cut (equal scores, which the rule orders by block index), when the
+// row takes the exact path.
 template <int E, bool RANKED, int MODE>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
                    uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
-                   float tau0, float tau1, float tau2, float tau3, RankFractions frac,
+                   uint32_t T0, uint32_t T1, uint32_t T2, uint32_t T3, RankFractions frac,
                    int q_block, int nqb, int causal) {
   constexpr int NP = 64 * E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -492,7 +501,7 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     s = wave_sum(s);
     inv_s = 1.0f / s;
   }
-  const float tau[4] = {tau0, tau1, tau2, tau3};
+  const uint32_t T[4] = {T0, T1, T2, T3};     // mass thresholds in mass units
   // ranked rule: K_l = floor(f_l * nvis) in double precision (the host's expression)
   int K[4];
 #pragma unroll
@@ -510,7 +519,8 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     }
   }
 
-  if (MODE == 1 || (MODE == 0 && cmass == nullptr)) {
+  static_assert(MODE == 2 || (MODE == 0 && RANKED), "the fast path is the ranked rule's");
+  if (MODE == 0 && cmass == nullptr) {
     uint32_t orig[E], key[E];
 #pragma unroll
     for (int r = 0; r < E; ++r) {
@@ -525,33 +535,10 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
     tie |= lane < 63 && key[E - 1] == next_first && key[E - 1] != kPadKey32;
     const bool any_tie = __ballot(tie) != 0;
-    // cnt[l]: how many blocks, in rank order, take level l or a finer one. Blocks with
-    // equal scores have equal masses, so the prefix sums along the sorted keys do not
-    // depend on how the sort ordered them among themselves.
-    int cnt[kMaxLevels] = {0, 0, 0, 0};
-    if constexpr (RANKED) {
+    // cnt[l]: how many blocks, in rank order, take level l or a finer one
+    int cnt[kMaxLevels];
 #pragma unroll
-      for (int l = 0; l < kMaxLevels; ++l) cnt[l] = K[l];
-    } else {
-      float p[E], tot = 0.f;
-#pragma unroll
-      for (int r = 0; r < E; ++r) {
-        p[r] = key[r] != kPadKey32 ? __expf(key32_score(key[r]) - mx) * inv_s : 0.f;
-        tot += p[r];
-      }
-      float run = wave_exclusive_sum(tot, lane);
-      int lc[kMaxLevels] = {0, 0, 0, 0};   // this lane's blocks with C below each threshold
-#pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const float C = run;
-        run += p[r];
-        const bool real = key[r] != kPadKey32;
-#pragma unroll
-        for (int l = 0; l < kMaxLevels; ++l) lc[l] += real && C < tau[l] ? 1 : 0;
-      }
-#pragma unroll
-      for (int l = 0; l < kMaxLevels; ++l) cnt[l] = (int)wave_sum((float)lc[l]);   // exact: counts < 2^24
-    }
+    for (int l = 0; l < kMaxLevels; ++l) cnt[l] = K[l];
     // cut[l]: key at sorted position cnt[l] - 1, the last block level l (or a finer one)
     // takes. Equal scores matter only where more than cnt[l] keys are <= cut[l], i.e. a
     // key after the cut equals it: then the index order decides which of them are in,
@@ -577,7 +564,6 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
       for (int l = 0; l < kMaxLevels; ++l)
         if (l < L && cnt[l] > 0) split |= (int)wave_sum((float)le[l]) > cnt[l];   // exact: counts < 2^24
     }
-    if (MODE == 1 && lane == 0) need_exact[row] = split ? 1 : 0;
     if (!split) {
 #pragma unroll
       for (int r = 0; r < E; ++r) {
@@ -593,7 +579,6 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
       }
       return;
     }
-    if constexpr (MODE == 1) return;
   }
 
   // ---- exact path: sort (score, index) keys
@@ -604,51 +589,231 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     key[r] = j < nvis ? rank_key(zz[r], j) : ~0ull;   // padding (and invisible blocks) sort last
   }
   wave_bitonic_sort<E>(key, lane);
-  float p[E], tot = 0.f;
+  uint32_t u[E], tot = 0u;
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const uint32_t j = (uint32_t)key[r];
-    p[r] = want_mass && j < (uint32_t)nvis ? __expf(key_score(key[r]) - mx) * inv_s : 0.f;
-    tot += p[r];
+    u[r] = want_mass && j < (uint32_t)nvis ? mass_units(__expf(key_score(key[r]) - mx) * inv_s) : 0u;
+    tot += u[r];
   }
-  float run = want_mass ? wave_exclusive_sum(tot, lane) : 0.f;
+  uint32_t run = want_mass ? wave_exclusive_sum_u32(tot, lane) : 0u;
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const uint32_t j = (uint32_t)key[r];
-    const float C = run;
-    run += p[r];
+    const uint32_t C = run;
+    run += u[r];
     if (j < (uint32_t)nvis) {
       int lev = -1;
 #pragma unroll
       for (int l = kMaxLevels - 1; l >= 0; --l) {
-        const bool in = RANKED ? E * lane + r < K[l] : C < tau[l];   // sorted position = rank
+        const bool in = RANKED ? E * lane + r < K[l] : C < T[l];   // sorted position = rank
         if (l < L && in) lev = l;
       }
       if (64 * (int)j < n_dense_prefix || (int)j >= dfirst) lev = 0;
       lrow[j] = (int8_t)lev;
-      if (crow) crow[j] = C;
+      if (crow) crow[j] = (float)C * (1.0f / kMassScale);
     }
   }
 }
 
-// Fast pass for long rows (more than 512 KV blocks), in place of the sort of the whole
-// padded row: a block ranked behind blocks holding at least tau_{L-1} of the mass (the
-// ranked rule: at least K_{L-1} blocks) can take no level, so a score cut x with
-// M(z > x) >= tau_{L-1} (plus a margin far above the float32 error of that sum) leaves out
-// only pruned blocks. Bisection on x finds one that keeps at most half the padded row
-// (32 E candidates); the candidates' 32-bit keys are compacted into LDS (wave-private) and
-// sorted, and the cuts come from their prefix masses exactly as in block_level_kernel's
-// fast path (the blocks ahead of a candidate are all candidates, so its mass ranked ahead
-// is complete). Rows where no such cut exists, or where a cut splits equal scores, are
-// flagged in need_exact for the exact pass. The row max and mass sum are taken in the
-// same grouping as block_level_kernel's (E consecutive blocks per lane), so every block's
-// mass is the same float.
-template <int E, bool RANKED>
+// Fast pass of the threshold rule (no cumulative mass asked), without a sort. The visible
+// scores go into NB buckets by their distance below the row's top score (bucket 0 holds
+// the top), with an integer mass histogram. Bucket order follows the rank order, so the
+// mass ranked ahead of a block of bucket b is F(b), the mass of the buckets before it,
+// plus that of the blocks of bucket b ranked ahead of it; for threshold l the last bucket
+// with F(b) < T_l holds the cut: every block of an earlier bucket takes level l or a finer
+// one and no block of a later bucket does. Only the blocks of those (at most four)
+// buckets are ranked exactly: their (score, index) keys are sorted across the wave, one
+// per lane, and their masses scanned in that order. A row whose cut buckets hold more than
+// 64 blocks is flagged in need_exact for block_level_kernel's exact pass. The masses are
+// the exact pass's integers, so the two passes give the same levels.
+template <int E>
+__global__ void __launch_bounds__(kMaskThreads)
+block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map,
+                       uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
+                       uint32_t T0, uint32_t T1, uint32_t T2, uint32_t T3, int q_block, int nqb, int causal) {
+  constexpr int NP = 64 * E;
+  constexpr int NB = 512;                   // buckets
+  constexpr int BPL = NB / 64;              // buckets per lane
+  __shared__ __align__(16) uint32_t hist[kMaskThreads / 64][NB];
+  __shared__ uint64_t cbuf[kMaskThreads / 64][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * (kMaskThreads / 64) + wave;
+  if (row >= nrows) return;                 // whole wave; wave-private LDS, no barrier
+  int nvis = nkb, dfirst = nkb;
+  if (causal) {
+    const int r0 = (row % nqb) * q_block;
+    nvis = (min(N, r0 + q_block) - 1) / 64 + 1;
+    dfirst = r0 / 64;
+  }
+  const float* zr = z + (int64_t)row * NP + E * lane;
+  float zz[E];
+  if constexpr (E >= 4) {
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {   // the row's scores only (groups of 4 stay in the padded row)
+      const float4 f = E * lane + 4 * c < nkb ? reinterpret_cast<const float4*>(zr)[c]
+                                              : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      zz[4 * c] = f.x; zz[4 * c + 1] = f.y; zz[4 * c + 2] = f.z; zz[4 * c + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < E; ++r) zz[r] = E * lane + r < nkb ? zr[r] : -INFINITY;
+  }
+  int8_t* lrow = level_map + (int64_t)row * nkb;
+  // softmax statistics in block_level_kernel's grouping, so every mass is the same float
+  float mx = -INFINITY, zmin = INFINITY;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int j = E * lane + r;
+    if (j < nvis) {
+      mx = fmaxf(mx, zz[r]);
+      zmin = fminf(zmin, zz[r]);
+    } else if (j < nkb) {
+      lrow[j] = -1;                         // causal: blocks after the query block
+    }
+  }
+  mx = wave_max(mx);
+  zmin = -wave_max(-zmin);
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    if (E * lane + r < nvis) s += __expf(zz[r] - mx);
+  s = wave_sum(s);
+  const float inv_s = 1.0f / s;
+  const float bscale = mx > zmin ? (float)NB / (mx - zmin) : 0.f;
+  auto bucket_of = [&](float zv) { return min(NB - 1, (int)((mx - zv) * bscale)); };
+
+  // ---- integer mass histogram over the buckets
+  uint32_t* h = hist[wave];
+#pragma unroll
+  for (int c = 0; c < BPL / 4; ++c) reinterpret_cast<uint4*>(h + BPL * lane)[c] = make_uint4(0u, 0u, 0u, 0u);
+  __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  int bk[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const bool vis = E * lane + r < nvis;
+    bk[r] = vis ? bucket_of(zz[r]) : NB;
+    const uint32_t u = vis ? mass_units(__expf(zz[r] - mx) * inv_s) : 0u;
+    if (u != 0u) atomicAdd(&hist[wave][bk[r]], u);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+  // F of this lane's buckets BPL*lane + k: an exclusive prefix in bucket order
+  uint32_t F[BPL];
+  {
+    uint32_t hv[BPL];
+#pragma unroll
+    for (int c = 0; c < BPL / 4; ++c) {
+      const uint4 v4 = reinterpret_cast<const uint4*>(h + BPL * lane)[c];
+      hv[4 * c] = v4.x; hv[4 * c + 1] = v4.y; hv[4 * c + 2] = v4.z; hv[4 * c + 3] = v4.w;
+    }
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      F[k] = tot;
+      tot += hv[k];
+    }
+    const uint32_t base = wave_exclusive_sum_u32(tot, lane);
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) F[k] += base;
+  }
+  const uint32_t T[kMaxLevels] = {T0, T1, T2, T3};
+  // cut bucket of each threshold: the last bucket with F < T (F is nondecreasing)
+  int dcut[kMaxLevels];
+  uint32_t Fcut[kMaxLevels];
+#pragma unroll
+  for (int l = 0; l < kMaxLevels; ++l) {
+    dcut[l] = -1;
+    Fcut[l] = 0u;
+    if (l < L && T[l] > 0u) {
+      int D = 0;
+#pragma unroll
+      for (int k = 0; k < BPL; ++k) D += __popcll(__ballot(F[k] < T[l]));
+      dcut[l] = D - 1;                      // >= 0: F(0) = 0 < T
+      uint32_t v = F[0];
+#pragma unroll
+      for (int k = 1; k < BPL; ++k)
+        if (dcut[l] % BPL == k) v = F[k];
+      Fcut[l] = (uint32_t)__builtin_amdgcn_readlane((int)v, dcut[l] / BPL);
+    }
+  }
+
+  // ---- the blocks of the cut buckets, ranked exactly (one per lane)
+  int ncand = 0;
+  uint64_t* cb = cbuf[wave];
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    bool c = false;
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) c |= bk[r] == dcut[l];
+    const uint64_t m = __ballot(c);
+    const int pos = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    if (c && pos < 64) cb[pos] = rank_key(zz[r], E * lane + r);
+    ncand += __popcll(m);
+  }
+  const bool fail = ncand > 64;
+  uint64_t kap[kMaxLevels];                 // key of the last block taking level l or finer
+  bool has[kMaxLevels];
+  if (!fail) {
+    if (lane >= ncand) cb[lane] = ~0ull;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    uint64_t ck[1] = {cb[lane]};
+    wave_bitonic_sort<1>(ck, lane);
+    const bool real = ck[0] != ~0ull;
+    const float zc = key_score(ck[0]);
+    const uint32_t uc = real ? mass_units(__expf(zc - mx) * inv_s) : 0u;
+    const int bc = real ? bucket_of(zc) : NB;
+    const uint32_t G = wave_exclusive_sum_u32(uc, lane);
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) {
+      has[l] = dcut[l] >= 0;
+      kap[l] = ~0ull;                       // an empty cut bucket (the last one): every block is in
+      if (!has[l]) continue;
+      const uint64_t mb = __ballot(bc == dcut[l]);
+      if (mb == 0) continue;
+      const int first = __builtin_ctzll(mb);
+      const uint32_t start = (uint32_t)__builtin_amdgcn_readlane((int)G, first);
+      const uint32_t C = Fcut[l] + (G - start);
+      const uint64_t mi = __ballot(bc == dcut[l] && C < T[l]);   // never empty: the first has C = F < T
+      const int last = 63 - __builtin_clzll(mi);
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ck[0], last);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(ck[0] >> 32), last);
+      kap[l] = ((uint64_t)hi << 32) | lo;
+    }
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int j = E * lane + r;
+      if (j < nvis) {
+        const uint64_t kr = rank_key(zz[r], j);
+        int lev = -1;
+#pragma unroll
+        for (int l = kMaxLevels - 1; l >= 0; --l)
+          if (has[l] && kr <= kap[l]) lev = l;
+        if (64 * j < n_dense_prefix || j >= dfirst) lev = 0;
+        lrow[j] = (int8_t)lev;
+      }
+    }
+  }
+  if (lane == 0) need_exact[row] = fail ? 1 : 0;
+}
+
+// Fast pass of the ranked rule for long rows (more than 512 KV blocks), in place of the
+// sort of the whole padded row: a block ranked behind K_{L-1} blocks takes no level, so a
+// score cut x with at least K_{L-1} blocks above it leaves out only pruned blocks.
+// Bisection on x finds one that keeps at most half the padded row (32 E candidates); the
+// candidates' 32-bit keys are compacted into LDS (wave-private) and sorted, and the cuts
+// come from the sorted positions K_l exactly as in block_level_kernel's fast path (the
+// blocks ahead of a candidate are all candidates, so its rank is complete). Rows where no
+// such cut exists, or where a cut splits equal scores, are flagged in need_exact for the
+// exact pass.
+template <int E>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map,
                         uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
-                        float tau0, float tau1, float tau2, float tau3, RankFractions frac, int q_block, int nqb,
-                        int causal) {
+                        RankFractions frac, int q_block, int nqb, int causal) {
   constexpr int NP = 64 * E;
   constexpr int EC = E / 2;                 // candidate keys per lane in the sort
   constexpr int kCand = 64 * EC;
@@ -682,26 +847,16 @@ block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_
     }
   }
   mx = wave_max(mx);
-  float ez[E], s = 0.f;
-#pragma unroll
-  for (int r = 0; r < E; ++r) {
-    ez[r] = E * lane + r < nvis ? __expf(zz[r] - mx) : 0.f;
-    s += ez[r];
-  }
-  s = wave_sum(s);
-  const float inv_s = 1.0f / s;
-  const float tau[4] = {tau0, tau1, tau2, tau3};
   int K[4];
 #pragma unroll
-  for (int l = 0; l < 4; ++l) K[l] = RANKED && l < L ? (int)floor(frac.f[l] * (double)nvis) : 0;
+  for (int l = 0; l < 4; ++l) K[l] = l < L ? (int)floor(frac.f[l] * (double)nvis) : 0;
 
   // ---- the score cut: every visible block when they fit, else bisection
   bool fail = false;
   float x = -INFINITY;
   if (nvis > kCand) {
-    const float T = tau[L - 1] + 2e-6f;     // mass that must lie above the cut (threshold rule)
-    const int Kt = K[L - 1];                // blocks that must lie above the cut (ranked rule)
-    fail = RANKED ? Kt > kCand : T > 0.999f;
+    const int Kt = K[L - 1];                // blocks that must lie above the cut
+    fail = Kt > kCand;
     float zmin = INFINITY;
 #pragma unroll
     for (int r = 0; r < E; ++r)
@@ -712,16 +867,10 @@ block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_
     for (int it = 0; it < 40 && !fail && !found; ++it) {
       const float mid = 0.5f * (lo + hi);
       if (!(mid > lo && mid < hi)) break;   // float resolution exhausted
-      float m = 0.f;
       int cnt = 0;
 #pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const bool above = zz[r] > mid;
-        m += above ? ez[r] : 0.f;
-        cnt += __popcll(__ballot(above));
-      }
-      const bool ok = RANKED ? cnt >= Kt : wave_sum(m) * inv_s >= T;
-      if (ok) {
+      for (int r = 0; r < E; ++r) cnt += __popcll(__ballot(zz[r] > mid));
+      if (cnt >= Kt) {
         lo = mid;
         found = cnt <= kCand;
       } else {
@@ -766,34 +915,10 @@ block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_
     const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
     tie |= lane < 63 && key[EC - 1] == next_first && key[EC - 1] != kPadKey32;
     const bool any_tie = __ballot(tie) != 0;
-    int cnt[kMaxLevels] = {0, 0, 0, 0};
-    if constexpr (RANKED) {
-#pragma unroll
-      for (int l = 0; l < kMaxLevels; ++l) cnt[l] = K[l];
-    } else {
-      float p[EC], tot = 0.f;
-#pragma unroll
-      for (int r = 0; r < EC; ++r) {
-        p[r] = key[r] != kPadKey32 ? __expf(key32_score(key[r]) - mx) * inv_s : 0.f;
-        tot += p[r];
-      }
-      float run = wave_exclusive_sum(tot, lane);
-      int lc[kMaxLevels] = {0, 0, 0, 0};
-#pragma unroll
-      for (int r = 0; r < EC; ++r) {
-        const float C = run;
-        run += p[r];
-        const bool real = key[r] != kPadKey32;
-#pragma unroll
-        for (int l = 0; l < kMaxLevels; ++l) lc[l] += real && C < tau[l] ? 1 : 0;
-      }
-#pragma unroll
-      for (int l = 0; l < kMaxLevels; ++l) cnt[l] = (int)wave_sum((float)lc[l]);   // exact: counts < 2^24
-    }
     uint32_t cut[kMaxLevels];
 #pragma unroll
     for (int l = 0; l < kMaxLevels; ++l) {
-      const int pos = cnt[l] - 1;
+      const int pos = K[l] - 1;
       uint32_t v = key[0];
 #pragma unroll
       for (int r = 1; r < EC; ++r)
@@ -811,7 +936,7 @@ block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_
       }
 #pragma unroll
       for (int l = 0; l < kMaxLevels; ++l)
-        if (l < L && cnt[l] > 0) fail |= (int)wave_sum((float)le[l]) > cnt[l];   // exact: counts < 2^24
+        if (l < L && K[l] > 0) fail |= (int)wave_sum((float)le[l]) > K[l];   // exact: counts < 2^24
     }
     if (!fail) {
 #pragma unroll
@@ -822,7 +947,7 @@ block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_
           int lev = -1;
 #pragma unroll
           for (int l = kMaxLevels - 1; l >= 0; --l)
-            if (l < L && cnt[l] > 0 && kr <= cut[l]) lev = l;
+            if (l < L && K[l] > 0 && kr <= cut[l]) lev = l;
           if (64 * j < n_dense_prefix || j >= dfirst) lev = 0;
           lrow[j] = (int8_t)lev;
         }
@@ -832,26 +957,42 @@ block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_
   if (lane == 0) need_exact[row] = fail ? 1 : 0;
 }
 
+// C * 2^-31 < tau  <=>  C < ceil(tau * 2^31) for an integer mass C (tau * 2^31 is exact in
+// double: tau is a float)
+static uint32_t mass_threshold(float tau) {
+  const double t = std::ceil((double)tau * 2147483648.0);
+  return t <= 0.0 ? 0u : t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+}
+
 template <int E, bool RANKED>
 static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
   RankFractions frac;
   for (int l = 0; l < kMaxLevels; ++l) frac.f[l] = a.frac[l];
+  uint32_t T[kMaxLevels];
+  for (int l = 0; l < kMaxLevels; ++l) T[l] = mass_threshold(a.tau[l]);
   const dim3 grid((nrows + 3) / 4);
   const int causal = a.causal ? 1 : 0;
-  if constexpr (E <= 8) {
-    hipLaunchKernelGGL((block_level_kernel<E, RANKED, 0>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
-                       a.cmass, nullptr, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0], a.tau[1], a.tau[2],
-                       a.tau[3], frac, a.q_block, a.nqb, causal);
-  } else {
-    // without cmass: the fast pass, then the exact pass over the rows it flagged
-    if (a.cmass == nullptr)
-      hipLaunchKernelGGL((block_level_cand_kernel<E, RANKED>), grid, dim3(kMaskThreads), 0, stream, a.z,
-                         a.level_map, a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, a.tau[0], a.tau[1],
-                         a.tau[2], a.tau[3], frac, a.q_block, a.nqb, causal);
-    hipLaunchKernelGGL((block_level_kernel<E, RANKED, 2>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
-                       a.cmass, a.cmass == nullptr ? a.need_exact : nullptr, a.N, a.nkb, nrows, a.L,
-                       a.n_dense_prefix, a.tau[0], a.tau[1], a.tau[2], a.tau[3], frac, a.q_block, a.nqb, causal);
+  uint8_t* flagged = nullptr;               // exact pass over these rows only (null: every row)
+  if (a.cmass == nullptr) {
+    if constexpr (!RANKED) {
+      hipLaunchKernelGGL((block_level_sel_kernel<E>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
+                         a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2], T[3],
+                         a.q_block, a.nqb, causal);
+      flagged = a.need_exact;
+    } else if constexpr (E > 8) {
+      hipLaunchKernelGGL((block_level_cand_kernel<E>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
+                         a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, frac, a.q_block, a.nqb, causal);
+      flagged = a.need_exact;
+    } else {
+      hipLaunchKernelGGL((block_level_kernel<E, true, 0>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
+                         nullptr, nullptr, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2], T[3], frac,
+                         a.q_block, a.nqb, causal);
+      return;
+    }
   }
+  hipLaunchKernelGGL((block_level_kernel<E, RANKED, 2>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
+                     a.cmass, flagged, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2], T[3], frac,
+                     a.q_block, a.nqb, causal);
 }
 
 template <int E>
