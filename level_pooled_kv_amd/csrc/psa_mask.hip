@@ -17,22 +17,22 @@
 //    workspace row of n_pad floats per query block.
 //  * qblock_score_kernel (rows of more than 512 KV blocks): both of the above in one
 //    pass, the mean queries kept in LDS, 16 x 16 score tiles per product.
-//  * block_level_kernel: one wave per query-block row: softmax of the row, a
-//    bitonic sort of score keys held in registers (n_pad / 64 per lane; partners
+//  * block_level_sel_kernel (threshold rule, no cumulative mass asked): one wave per
+//    query-block row: softmax of the row into integer masses, a mass histogram over
+//    buckets of the score, and an exact ranking of only the blocks of the buckets that
+//    hold the cuts; rows it cannot settle are flagged for block_level_kernel's exact pass.
+//  * block_level_kernel: one wave per query-block row: softmax of the row, a bitonic
+//    sort of 64-bit (score, index) keys held in registers (n_pad / 64 per lane; partners
 //    in other lanes come through cross-lane shuffles, so no LDS and no workgroup
-//    barrier), a wave-wide exclusive scan of the masses in rank order, the
-//    threshold compares and the int8 level writes. 32-bit keys settle a row unless
-//    a cut splits a group of equal scores; such rows, and calls that want the
-//    cumulative mass, sort 64-bit (score, index) keys.
-//  * block_level_cand_kernel (rows of more than 512 KV blocks, no cumulative mass
-//    asked): a score cut found by bisection leaves out only blocks that take no level,
-//    and only the candidates above it are sorted; rows it cannot settle are flagged for
-//    block_level_kernel's exact pass.
-//    Its ranked form (the quantile rule the top168.com ablation compares with
-//    thresholds; fixed shares of the score-ranked blocks per level: skillmd.com,
-//    "Level assignment") gives the block at rank r the lowest level l with
-//    r < K_l for host-computed cumulative counts K_l, so it needs the sort but
-//    neither the softmax nor the scan.
+//    barrier), a wave-wide exclusive scan of the integer masses in rank order, the
+//    threshold compares and the int8 level writes (and the cumulative mass when asked).
+//  * The ranked rule (the quantile rule the top168.com ablation compares with
+//    thresholds; fixed shares of the score-ranked blocks per level: skillmd.com, "Level
+//    assignment") gives the block at rank r the lowest level l with r < K_l for
+//    host-computed cumulative counts K_l, so it needs the ranking but neither the softmax
+//    nor the scan: block_level_kernel sorts 32-bit score keys first (exact pass only where
+//    a cut splits equal scores); for rows of more than 512 KV blocks,
+//    block_level_cand_kernel sorts only the blocks above a score cut found by bisection.
 #include "psa_device.h"
 #include "psa_launch.h"
 

@@ -198,6 +198,32 @@ def test_mask_equal_scores(psa):
     check_mask(lev.cpu().numpy(), ora["mask"], tau, 4, 0, label="equal scores")
 
 
+@pytest.mark.parametrize("N,tau", [(4096, (0.05, 0.2, 0.4, 0.6)), (30000, (0.02, 0.08, 0.2, 0.5))],
+                         ids=["64 blocks", "469 blocks"])
+def test_mask_equal_scores_split_by_cut(psa, N, tau):
+    # 20 identical KV blocks: a group of equal scores small enough for the fast pass to
+    # rank exactly (their bucket holds at most 64 blocks), split by a threshold in some
+    # rows, where the block index decides; fast pass, exact pass and oracle must agree.
+    d, L = 64, 4
+    q, k, v = random_qkv(N // 100 + 3, 1, 2, 2, N, d, "bf16")
+    k[:, :, 64:64 * 21] = np.tile(k[:, :, 64:128], (1, 1, 20, 1))
+    ora = o.estimate_mask(q, k, 128, 64, tau, L, 1 / math.sqrt(d))
+    C = ora["cmass"][..., 1:21]
+    split = sum(int(np.sum((C < t).any(-1) & (C >= t).any(-1))) for t in tau)
+    assert split > 0, "no threshold falls inside the group of equal scores"
+    prob = psa.Problem(B=1, H=2, H_kv=2, N=N, d=d, q_block=128, num_levels=L, dtype="bf16")
+    say(f"mask with 20 equal-score blocks split by a cut in {split} row-thresholds, N={N}")
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    _, _, kbar = psa.psa_build_pyramid(prob, kd, to_device(v, "bf16"))
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, tau)
+    lev_c, cm_c = psa.psa_estimate_mask(prob, qd, kbar, tau, want_cmass=True)
+    torch.cuda.synchronize()
+    lev_g = lev.cpu().numpy()
+    check_fast_vs_exact(lev_g, lev_c.cpu().numpy(), to_host(cm_c), tau, L, label=f"20 equal scores, N={N}")
+    check_mask(lev_g, ora, tau, L, 0, label=f"20 equal scores, N={N}")
+    check_cmass(to_host(cm_c), ora, label=f"20 equal scores, N={N}")
+
+
 @pytest.mark.parametrize("N", [40000, 70000], ids=["625 blocks", "1094 blocks"])
 def test_mask_equal_scores_long_rows(psa, N):
     # Rows of more than 512 KV blocks run as a fast kernel and an exact kernel over the
