@@ -20,7 +20,8 @@
 //  * block_level_sel_kernel (threshold rule, no cumulative mass asked): one wave per
 //    query-block row: softmax of the row into integer masses, a mass histogram over
 //    buckets of the score, and an exact ranking of only the blocks of the buckets that
-//    hold the cuts; rows it cannot settle are flagged for block_level_kernel's exact pass.
+//    hold the cuts; a row it cannot settle takes the exact sort (in the same kernel for
+//    rows of up to 512 blocks, in block_level_kernel's exact pass for longer ones).
 //  * block_level_kernel: one wave per query-block row: softmax of the row, a bitonic
 //    sort of 64-bit (score, index) keys held in registers (n_pad / 64 per lane; partners
 //    in other lanes come through cross-lane shuffles, so no LDS and no workgroup
@@ -444,9 +445,11 @@ __device__ __forceinline__ uint32_t wave_exclusive_sum_u32(uint32_t tot, int lan
 // One wave per query-block row. Exact path: sort 64-bit (score, index) keys, scan the
 // integer masses in rank order and compare them with the thresholds (the ranked rule:
 // compare the sorted position with K_l), writing the cumulative mass when asked. MODE 2
-// runs it over the rows flagged in need_exact (every row when need_exact is null), after
-// a fast pass: block_level_sel_kernel for the threshold rule, block_level_cand_kernel for
-// the ranked rule on rows of more than 512 blocks. MODE 0 (ranked rule, shorter rows)
+// runs it over the rows flagged in need_exact (every row when need_exact is null): after
+// block_level_cand_kernel (ranked rule) or block_level_sel_kernel (threshold rule) on rows
+// of more than 512 blocks, or over every row when the cumulative mass is asked for
+// (block_level_sel_kernel runs the same exact path itself for the shorter rows it cannot
+// settle). MODE 0 (ranked rule, shorter rows)
 // first tries the fast path in this kernel: sort the 32-bit score keys; level l takes the
 // blocks whose key is at most the key at sorted position K_l - 1, unless that key
 // continues past the cut (equal scores, which the rule orders by block index), when the
@@ -616,6 +619,43 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
   }
 }
 
+// Levels of one row by the threshold rule from a sort of its (score, index) keys: the
+// exact pass of block_level_kernel for a row the bucket pass could not settle.
+template <int E>
+__device__ __forceinline__ void exact_threshold_levels(const float (&zz)[E], float mx, float inv_s, int nvis,
+                                                       int dfirst, int8_t* lrow, const uint32_t (&T)[kMaxLevels],
+                                                       int L, int n_dense_prefix, int lane) {
+  uint64_t key[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int j = E * lane + r;
+    key[r] = j < nvis ? rank_key(zz[r], j) : ~0ull;
+  }
+  wave_bitonic_sort<E>(key, lane);
+  uint32_t u[E], tot = 0u;
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const uint32_t j = (uint32_t)key[r];
+    u[r] = j < (uint32_t)nvis ? mass_units(__expf(key_score(key[r]) - mx) * inv_s) : 0u;
+    tot += u[r];
+  }
+  uint32_t run = wave_exclusive_sum_u32(tot, lane);
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const uint32_t j = (uint32_t)key[r];
+    const uint32_t C = run;
+    run += u[r];
+    if (j < (uint32_t)nvis) {
+      int lev = -1;
+#pragma unroll
+      for (int l = kMaxLevels - 1; l >= 0; --l)
+        if (l < L && C < T[l]) lev = l;
+      if (64 * (int)j < n_dense_prefix || (int)j >= dfirst) lev = 0;
+      lrow[j] = (int8_t)lev;
+    }
+  }
+}
+
 // Fast pass of the threshold rule (no cumulative mass asked), without a sort. The visible
 // scores go into NB buckets by their distance below the row's top score (bucket 0 holds
 // the top), with an integer mass histogram. Bucket order follows the rank order, so the
@@ -625,8 +665,10 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
 // one and no block of a later bucket does. Only the blocks of those (at most four)
 // buckets are ranked exactly: their (score, index) keys are sorted across the wave, one
 // per lane, and their masses scanned in that order. A row whose cut buckets hold more than
-// 64 blocks is flagged in need_exact for block_level_kernel's exact pass. The masses are
-// the exact pass's integers, so the two passes give the same levels.
+// 64 blocks (many equal scores) takes the exact pass's sort of the whole row: here for rows
+// of up to 512 blocks, in block_level_kernel's exact pass (flagged in need_exact) for
+// longer ones, whose sort would weigh on every row of this kernel. The masses are the
+// exact pass's integers, so all ways give the same levels.
 template <int E>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map,
@@ -797,7 +839,11 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
       }
     }
   }
-  if (lane == 0) need_exact[row] = fail ? 1 : 0;
+  if constexpr (E <= 8) {
+    if (fail) exact_threshold_levels<E>(zz, mx, inv_s, nvis, dfirst, lrow, T, L, n_dense_prefix, lane);
+  } else {
+    if (lane == 0) need_exact[row] = fail ? 1 : 0;
+  }
 }
 
 // Fast pass of the ranked rule for long rows (more than 512 KV blocks), in place of the
@@ -978,6 +1024,7 @@ static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
       hipLaunchKernelGGL((block_level_sel_kernel<E>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
                          a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2], T[3],
                          a.q_block, a.nqb, causal);
+      if constexpr (E <= 8) return;          // unsettled rows were sorted in the kernel
       flagged = a.need_exact;
     } else if constexpr (E > 8) {
       hipLaunchKernelGGL((block_level_cand_kernel<E>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
