@@ -20,6 +20,13 @@ __device__ __forceinline__ U128 ld128(const void* p) {
   uint4 v = *reinterpret_cast<const uint4*>(p);
   U128 r; r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w; return r;
 }
+// 16-byte load marked nontemporal (streaming): for data read once, so that the caches do
+// not give its lines priority over the lines later steps read.
+__device__ __forceinline__ U128 ld128_stream(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  U128 r; r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3]; return r;
+}
 __device__ __forceinline__ void st128(void* p, const U128& r) {
   *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
 }

@@ -10,7 +10,7 @@
 //
 // Kernels:
 //  * qblock_mean_kernel streams Q once (HBM-bound: every load of a thread is in
-//    flight at once, 16-byte loads, whole rows per wave, two query blocks per
+//    flight at once, 16-byte nontemporal loads, whole rows per wave, two query blocks per
 //    workgroup) and writes the float32 mean query of each query block to the workspace.
 //  * block_score_kernel: z = scale * qbar kbar^T + ln n_j per head on the float32
 //    matrix cores (v_mfma_f32_32x32x2_f32), one 32 x 32 tile per wave, into a
@@ -65,7 +65,7 @@ qblock_mean_kernel(const T* __restrict__ q, float* __restrict__ qbar, int N, int
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
       const int row = g + r * G;
-      raw[u][r] = row < m ? ld128(src + (int64_t)row * D) : U128{{0u, 0u, 0u, 0u}};
+      raw[u][r] = row < m ? ld128_stream(src + (int64_t)row * D) : U128{{0u, 0u, 0u, 0u}};
     }
   }
 #pragma unroll
@@ -220,7 +220,7 @@ qblock_score_kernel(const T* __restrict__ q, const float* __restrict__ kbar, flo
 #pragma unroll
     for (int k = 0; k < MAXR; ++k) {
       const int row = grp + k * G;
-      raw[k] = row < m ? ld128(qh + (int64_t)(r0 + row) * D) : U128{{0u, 0u, 0u, 0u}};
+      raw[k] = row < m ? ld128_stream(qh + (int64_t)(r0 + row) * D) : U128{{0u, 0u, 0u, 0u}};
     }
   };
   U128 buf[2][MAXR];
