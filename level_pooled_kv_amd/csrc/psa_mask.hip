@@ -17,11 +17,11 @@
 //    workspace row of n_pad floats per query block.
 //  * qblock_score_kernel (rows of more than 512 KV blocks): both of the above in one
 //    pass, the mean queries kept in LDS, 16 x 16 score tiles per product.
-//  * block_level_sel_kernel (threshold rule, no cumulative mass asked): one wave per
-//    query-block row: softmax of the row into integer masses, a mass histogram over
-//    buckets of the score, and an exact ranking of only the blocks of the buckets that
-//    hold the cuts; a row it cannot settle takes the exact sort (in the same kernel for
-//    rows of up to 512 blocks, in block_level_kernel's exact pass for longer ones).
+//  * block_level_sel_kernel (no cumulative mass asked): one wave per query-block row:
+//    a histogram of the blocks' weights (integer masses from the softmax of the row, or 1
+//    under the ranked rule) over buckets of the score, and an exact ranking of only the
+//    blocks of the buckets that hold the cuts; a row it cannot settle takes the exact sort
+//    (in the same kernel for rows of up to 512 blocks, in block_level_kernel for longer).
 //  * block_level_kernel: one wave per query-block row: softmax of the row, a bitonic
 //    sort of 64-bit (score, index) keys held in registers (n_pad / 64 per lane; partners
 //    in other lanes come through cross-lane shuffles, so no LDS and no workgroup
@@ -30,10 +30,7 @@
 //  * The ranked rule (the quantile rule the top168.com ablation compares with
 //    thresholds; fixed shares of the score-ranked blocks per level: skillmd.com, "Level
 //    assignment") gives the block at rank r the lowest level l with r < K_l for
-//    host-computed cumulative counts K_l, so it needs the ranking but neither the softmax
-//    nor the scan: block_level_kernel sorts 32-bit score keys first (exact pass only where
-//    a cut splits equal scores); for rows of more than 512 KV blocks,
-//    block_level_cand_kernel sorts only the blocks above a score cut found by bisection.
+//    host-computed cumulative counts K_l: the same passes with rank in place of mass.
 #include "psa_device.h"
 #include "psa_launch.h"
 
@@ -374,55 +371,6 @@ __device__ __forceinline__ void wave_bitonic_sort(uint64_t (&key)[E], int lane) 
   }
 }
 
-// 32-bit keys: the order word alone (no index). Exchanges are v_med3_u32 against 0
-// (minimum) or ~0 (maximum), one VALU op per element of a cross-lane stage.
-__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
-  return min(max(a, b), max(min(a, b), c));
-}
-__device__ __forceinline__ uint32_t score_key(float z) {
-  const uint32_t u = __float_as_uint(z + 0.0f);
-  return (u & 0x80000000u) ? u : (~u & 0x7fffffffu);
-}
-__device__ __forceinline__ float key32_score(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? key : (~key & 0x7fffffffu));
-}
-constexpr uint32_t kPadKey32 = 0xFFFFFFFFu;   // above every finite score's key
-
-template <int E, int M>
-__device__ __forceinline__ void stage_cross32(uint32_t (&key)[E], int lane, int k) {
-  const bool upper = (lane & M) != 0;
-  const bool asc = ((E * lane) & k) == 0;
-  const uint32_t c = (upper == asc) ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-  for (int r = 0; r < E; ++r) key[r] = med3u(key[r], xor_lane<M>(key[r], lane), c);
-}
-template <int E, int J>
-__device__ __forceinline__ void stage_in32(uint32_t (&key)[E], int lane, int k) {
-#pragma unroll
-  for (int r = 0; r < E; ++r) {
-    if (r & J) continue;
-    const uint32_t clo = ((E * lane + r) & k) == 0 ? 0u : 0xFFFFFFFFu;
-    const uint32_t a = key[r], b = key[r + J];
-    key[r] = med3u(a, b, clo);
-    key[r + J] = med3u(a, b, ~clo);
-  }
-}
-template <int E, int K, int J>
-__device__ __forceinline__ void merge32(uint32_t (&key)[E], int lane) {
-  if constexpr (J > 0) {
-    if constexpr (J >= E) stage_cross32<E, J / E>(key, lane, K);
-    else stage_in32<E, J>(key, lane, K);
-    merge32<E, K, J / 2>(key, lane);
-  }
-}
-template <int E, int K = 2>
-__device__ __forceinline__ void wave_bitonic_sort32(uint32_t (&key)[E], int lane) {
-  if constexpr (K <= 64 * E) {
-    merge32<E, K, K / 2>(key, lane);
-    wave_bitonic_sort32<E, 2 * K>(key, lane);
-  }
-}
-
 // Block masses in fixed point: p * 2^31 rounded to an integer (p <= 1, and the masses of
 // a row add up to about 2^31, so every partial sum fits 32 bits). Integer sums do not
 // depend on the order of the additions, so every pass (sorted scan, bucket histogram)
@@ -442,19 +390,13 @@ __device__ __forceinline__ uint32_t wave_exclusive_sum_u32(uint32_t tot, int lan
   return incl - tot;
 }
 
-// One wave per query-block row. Exact path: sort 64-bit (score, index) keys, scan the
-// integer masses in rank order and compare them with the thresholds (the ranked rule:
-// compare the sorted position with K_l), writing the cumulative mass when asked. MODE 2
-// runs it over the rows flagged in need_exact (every row when need_exact is null): after
-// block_level_cand_kernel (ranked rule) or block_level_sel_kernel (threshold rule) on rows
-// of more than 512 blocks, or over every row when the cumulative mass is asked for
-// (block_level_sel_kernel runs the same exact path itself for the shorter rows it cannot
-// settle). MODE 0 (ranked rule, shorter rows)
-// first tries the fast path in this kernel: sort the 32-bit score keys; level l takes the
-// blocks whose key is at most the key at sorted position K_l - 1, unless that key
-// continues past the cut (equal scores, which the rule orders by block index), when the
-// row takes the exact path.
-template <int E, bool RANKED, int MODE>
+// Exact level pass, one wave per query-block row: a sort of the row's 64-bit (score,
+// index) keys, a scan of the integer masses in rank order and the threshold compares (the
+// ranked rule: the sorted position against K_l), writing the cumulative mass when asked.
+// It runs over the rows flagged in need_exact by block_level_sel_kernel (rows of more
+// than 512 blocks it could not settle; it sorts shorter ones itself), or over every row
+// (need_exact null) when the cumulative mass is asked for.
+template <int E, bool RANKED>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
                    uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
@@ -464,9 +406,7 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * (kMaskThreads / 64) + wave;
   if (row >= nrows) return;                 // whole wave; no barrier in this kernel
-  if constexpr (MODE == 2) {
-    if (need_exact != nullptr && need_exact[row] == 0) return;
-  }
+  if (need_exact != nullptr && need_exact[row] == 0) return;
   // Causal use: the row ranks only the nvis blocks that hold a token at or before its
   // query block's last row; blocks from dfirst on reach the block's own rows and stay at
   // full resolution (a pooled key would mix in later tokens); later blocks are pruned.
@@ -522,68 +462,6 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     }
   }
 
-  static_assert(MODE == 2 || (MODE == 0 && RANKED), "the fast path is the ranked rule's");
-  if (MODE == 0 && cmass == nullptr) {
-    uint32_t orig[E], key[E];
-#pragma unroll
-    for (int r = 0; r < E; ++r) {
-      orig[r] = E * lane + r < nvis ? score_key(zz[r]) : kPadKey32;
-      key[r] = orig[r];
-    }
-    wave_bitonic_sort32<E>(key, lane);
-    // equal scores anywhere in the row (neighbours in sorted order)?
-    bool tie = false;
-#pragma unroll
-    for (int r = 0; r + 1 < E; ++r) tie |= key[r] == key[r + 1] && key[r] != kPadKey32;
-    const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
-    tie |= lane < 63 && key[E - 1] == next_first && key[E - 1] != kPadKey32;
-    const bool any_tie = __ballot(tie) != 0;
-    // cnt[l]: how many blocks, in rank order, take level l or a finer one
-    int cnt[kMaxLevels];
-#pragma unroll
-    for (int l = 0; l < kMaxLevels; ++l) cnt[l] = K[l];
-    // cut[l]: key at sorted position cnt[l] - 1, the last block level l (or a finer one)
-    // takes. Equal scores matter only where more than cnt[l] keys are <= cut[l], i.e. a
-    // key after the cut equals it: then the index order decides which of them are in,
-    // and the row takes the exact path.
-    uint32_t cut[kMaxLevels];
-#pragma unroll
-    for (int l = 0; l < kMaxLevels; ++l) {
-      const int pos = cnt[l] - 1;
-      uint32_t v = key[0];
-#pragma unroll
-      for (int r = 1; r < E; ++r)
-        if (pos >= 0 && pos % E == r) v = key[r];
-      cut[l] = pos >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v, pos / E) : 0u;
-    }
-    bool split = false;
-    if (any_tie) {
-      int le[kMaxLevels] = {0, 0, 0, 0};
-#pragma unroll
-      for (int r = 0; r < E; ++r)
-#pragma unroll
-        for (int l = 0; l < kMaxLevels; ++l) le[l] += orig[r] <= cut[l] ? 1 : 0;
-#pragma unroll
-      for (int l = 0; l < kMaxLevels; ++l)
-        if (l < L && cnt[l] > 0) split |= (int)wave_sum((float)le[l]) > cnt[l];   // exact: counts < 2^24
-    }
-    if (!split) {
-#pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const int j = E * lane + r;
-        if (j < nvis) {
-          int lev = -1;
-#pragma unroll
-          for (int l = kMaxLevels - 1; l >= 0; --l)
-            if (l < L && cnt[l] > 0 && orig[r] <= cut[l]) lev = l;
-          if (64 * j < n_dense_prefix || j >= dfirst) lev = 0;
-          lrow[j] = (int8_t)lev;
-        }
-      }
-      return;
-    }
-  }
-
   // ---- exact path: sort (score, index) keys
   uint64_t key[E];
 #pragma unroll
@@ -619,12 +497,13 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
   }
 }
 
-// Levels of one row by the threshold rule from a sort of its (score, index) keys: the
-// exact pass of block_level_kernel for a row the bucket pass could not settle.
-template <int E>
-__device__ __forceinline__ void exact_threshold_levels(const float (&zz)[E], float mx, float inv_s, int nvis,
-                                                       int dfirst, int8_t* lrow, const uint32_t (&T)[kMaxLevels],
-                                                       int L, int n_dense_prefix, int lane) {
+// Levels of one row from a sort of its (score, index) keys: the exact pass of
+// block_level_kernel for a row the bucket pass could not settle. A block's weight is its
+// integer mass (threshold rule) or 1 (ranked rule: the weight ranked ahead is the rank).
+template <int E, bool RANKED>
+__device__ __forceinline__ void exact_row_levels(const float (&zz)[E], float mx, float inv_s, int nvis,
+                                                 int dfirst, int8_t* lrow, const uint32_t (&T)[kMaxLevels],
+                                                 int L, int n_dense_prefix, int lane) {
   uint64_t key[E];
 #pragma unroll
   for (int r = 0; r < E; ++r) {
@@ -636,7 +515,7 @@ __device__ __forceinline__ void exact_threshold_levels(const float (&zz)[E], flo
 #pragma unroll
   for (int r = 0; r < E; ++r) {
     const uint32_t j = (uint32_t)key[r];
-    u[r] = j < (uint32_t)nvis ? mass_units(__expf(key_score(key[r]) - mx) * inv_s) : 0u;
+    u[r] = j < (uint32_t)nvis ? (RANKED ? 1u : mass_units(__expf(key_score(key[r]) - mx) * inv_s)) : 0u;
     tot += u[r];
   }
   uint32_t run = wave_exclusive_sum_u32(tot, lane);
@@ -656,24 +535,27 @@ __device__ __forceinline__ void exact_threshold_levels(const float (&zz)[E], flo
   }
 }
 
-// Fast pass of the threshold rule (no cumulative mass asked), without a sort. The visible
-// scores go into NB buckets by their distance below the row's top score (bucket 0 holds
-// the top), with an integer mass histogram. Bucket order follows the rank order, so the
-// mass ranked ahead of a block of bucket b is F(b), the mass of the buckets before it,
-// plus that of the blocks of bucket b ranked ahead of it; for threshold l the last bucket
-// with F(b) < T_l holds the cut: every block of an earlier bucket takes level l or a finer
-// one and no block of a later bucket does. Only the blocks of those (at most four)
-// buckets are ranked exactly: their (score, index) keys are sorted across the wave, one
-// per lane, and their masses scanned in that order. A row whose cut buckets hold more than
-// 64 blocks (many equal scores) takes the exact pass's sort of the whole row: here for rows
-// of up to 512 blocks, in block_level_kernel's exact pass (flagged in need_exact) for
-// longer ones, whose sort would weigh on every row of this kernel. The masses are the
-// exact pass's integers, so all ways give the same levels.
-template <int E>
+// Fast level pass (no cumulative mass asked), without a sort. The visible scores go into
+// NB buckets by their distance below the row's top score (bucket 0 holds the top), with a
+// histogram of the blocks' weights: their integer masses (threshold rule), or 1 (ranked
+// rule, where the weight ranked ahead of a block is its rank). Bucket order follows the
+// rank order, so the weight ranked ahead of a block of bucket b is F(b), the weight of the
+// buckets before it, plus that of the blocks of bucket b ranked ahead of it; for level l
+// (T_l: the mass threshold in mass units, or K_l blocks) the last bucket with F(b) < T_l
+// holds the cut: every block of an earlier bucket takes level l or a finer one and no
+// block of a later bucket does. Only the blocks of those (at most four) buckets are ranked
+// exactly: their (score, index) keys are sorted across the wave, one per lane, and their
+// weights scanned in that order. A row whose cut buckets hold more than 64 blocks (many
+// equal scores) takes the exact pass's sort of the whole row: here for rows of up to 512
+// blocks, in block_level_kernel's exact pass (flagged in need_exact) for longer ones,
+// whose sort would weigh on every row of this kernel. The weights are the exact pass's
+// integers, so all ways give the same levels.
+template <int E, bool RANKED>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map,
                        uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
-                       uint32_t T0, uint32_t T1, uint32_t T2, uint32_t T3, int q_block, int nqb, int causal) {
+                       uint32_t T0, uint32_t T1, uint32_t T2, uint32_t T3, RankFractions frac, int q_block,
+                       int nqb, int causal) {
   constexpr int NP = 64 * E;
   constexpr int NB = 512;                   // buckets
   constexpr int BPL = NB / 64;              // buckets per lane
@@ -716,16 +598,21 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
   }
   mx = wave_max(mx);
   zmin = -wave_max(-zmin);
-  float s = 0.f;
+  float inv_s = 0.f;
+  if constexpr (!RANKED) {
+    float s = 0.f;
 #pragma unroll
-  for (int r = 0; r < E; ++r)
-    if (E * lane + r < nvis) s += __expf(zz[r] - mx);
-  s = wave_sum(s);
-  const float inv_s = 1.0f / s;
+    for (int r = 0; r < E; ++r)
+      if (E * lane + r < nvis) s += __expf(zz[r] - mx);
+    s = wave_sum(s);
+    inv_s = 1.0f / s;
+  }
   const float bscale = mx > zmin ? (float)NB / (mx - zmin) : 0.f;
   auto bucket_of = [&](float zv) { return min(NB - 1, (int)((mx - zv) * bscale)); };
+  // a visible block's weight: its integer mass, or 1 (ranked rule)
+  auto weight_of = [&](float zv) { return RANKED ? 1u : mass_units(__expf(zv - mx) * inv_s); };
 
-  // ---- integer mass histogram over the buckets
+  // ---- weight histogram over the buckets
   uint32_t* h = hist[wave];
 #pragma unroll
   for (int c = 0; c < BPL / 4; ++c) reinterpret_cast<uint4*>(h + BPL * lane)[c] = make_uint4(0u, 0u, 0u, 0u);
@@ -736,7 +623,7 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
   for (int r = 0; r < E; ++r) {
     const bool vis = E * lane + r < nvis;
     bk[r] = vis ? bucket_of(zz[r]) : NB;
-    const uint32_t u = vis ? mass_units(__expf(zz[r] - mx) * inv_s) : 0u;
+    const uint32_t u = vis ? weight_of(zz[r]) : 0u;
     if (u != 0u) atomicAdd(&hist[wave][bk[r]], u);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -760,7 +647,11 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
 #pragma unroll
     for (int k = 0; k < BPL; ++k) F[k] += base;
   }
-  const uint32_t T[kMaxLevels] = {T0, T1, T2, T3};
+  uint32_t T[kMaxLevels] = {T0, T1, T2, T3};
+  if constexpr (RANKED) {   // K_l = floor(f_l * nvis) in double precision (the host's expression)
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) T[l] = l < L ? (uint32_t)floor(frac.f[l] * (double)nvis) : 0u;
+  }
   // cut bucket of each threshold: the last bucket with F < T (F is nondecreasing)
   int dcut[kMaxLevels];
   uint32_t Fcut[kMaxLevels];
@@ -806,7 +697,7 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
     wave_bitonic_sort<1>(ck, lane);
     const bool real = ck[0] != ~0ull;
     const float zc = key_score(ck[0]);
-    const uint32_t uc = real ? mass_units(__expf(zc - mx) * inv_s) : 0u;
+    const uint32_t uc = real ? weight_of(zc) : 0u;
     const int bc = real ? bucket_of(zc) : NB;
     const uint32_t G = wave_exclusive_sum_u32(uc, lane);
 #pragma unroll
@@ -840,167 +731,10 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
     }
   }
   if constexpr (E <= 8) {
-    if (fail) exact_threshold_levels<E>(zz, mx, inv_s, nvis, dfirst, lrow, T, L, n_dense_prefix, lane);
+    if (fail) exact_row_levels<E, RANKED>(zz, mx, inv_s, nvis, dfirst, lrow, T, L, n_dense_prefix, lane);
   } else {
     if (lane == 0) need_exact[row] = fail ? 1 : 0;
   }
-}
-
-// Fast pass of the ranked rule for long rows (more than 512 KV blocks), in place of the
-// sort of the whole padded row: a block ranked behind K_{L-1} blocks takes no level, so a
-// score cut x with at least K_{L-1} blocks above it leaves out only pruned blocks.
-// Bisection on x finds one that keeps at most half the padded row (32 E candidates); the
-// candidates' 32-bit keys are compacted into LDS (wave-private) and sorted, and the cuts
-// come from the sorted positions K_l exactly as in block_level_kernel's fast path (the
-// blocks ahead of a candidate are all candidates, so its rank is complete). Rows where no
-// such cut exists, or where a cut splits equal scores, are flagged in need_exact for the
-// exact pass.
-template <int E>
-__global__ void __launch_bounds__(kMaskThreads)
-block_level_cand_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map,
-                        uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
-                        RankFractions frac, int q_block, int nqb, int causal) {
-  constexpr int NP = 64 * E;
-  constexpr int EC = E / 2;                 // candidate keys per lane in the sort
-  constexpr int kCand = 64 * EC;
-  __shared__ __align__(16) uint32_t cbuf[kMaskThreads / 64][kCand];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.x * (kMaskThreads / 64) + wave;
-  if (row >= nrows) return;                 // whole wave; wave-private LDS, no barrier
-  int nvis = nkb, dfirst = nkb;
-  if (causal) {
-    const int r0 = (row % nqb) * q_block;
-    nvis = (min(N, r0 + q_block) - 1) / 64 + 1;
-    dfirst = r0 / 64;
-  }
-  const float* zr = z + (int64_t)row * NP + E * lane;
-  float zz[E];
-#pragma unroll
-  for (int c = 0; c < E / 4; ++c) {   // the row's scores only, not its padding (groups of 4 stay in the row)
-    const float4 f = E * lane + 4 * c < nkb ? reinterpret_cast<const float4*>(zr)[c]
-                                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    zz[4 * c] = f.x; zz[4 * c + 1] = f.y; zz[4 * c + 2] = f.z; zz[4 * c + 3] = f.w;
-  }
-  int8_t* lrow = level_map + (int64_t)row * nkb;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < E; ++r) {
-    const int j = E * lane + r;
-    if (j < nvis) mx = fmaxf(mx, zz[r]);
-    else {
-      if (j < nkb) lrow[j] = -1;            // causal: blocks after the query block
-      zz[r] = -INFINITY;                    // never a candidate
-    }
-  }
-  mx = wave_max(mx);
-  int K[4];
-#pragma unroll
-  for (int l = 0; l < 4; ++l) K[l] = l < L ? (int)floor(frac.f[l] * (double)nvis) : 0;
-
-  // ---- the score cut: every visible block when they fit, else bisection
-  bool fail = false;
-  float x = -INFINITY;
-  if (nvis > kCand) {
-    const int Kt = K[L - 1];                // blocks that must lie above the cut
-    fail = Kt > kCand;
-    float zmin = INFINITY;
-#pragma unroll
-    for (int r = 0; r < E; ++r)
-      if (E * lane + r < nvis) zmin = fminf(zmin, zz[r]);
-    zmin = -wave_max(-zmin);
-    float lo = zmin - 1.0f, hi = mx;        // lo: a valid cut (every visible block above it)
-    bool found = false;
-    for (int it = 0; it < 40 && !fail && !found; ++it) {
-      const float mid = 0.5f * (lo + hi);
-      if (!(mid > lo && mid < hi)) break;   // float resolution exhausted
-      int cnt = 0;
-#pragma unroll
-      for (int r = 0; r < E; ++r) cnt += __popcll(__ballot(zz[r] > mid));
-      if (cnt >= Kt) {
-        lo = mid;
-        found = cnt <= kCand;
-      } else {
-        hi = mid;
-      }
-    }
-    fail = fail || !found;
-    x = lo;
-  }
-
-  // ---- compact the candidates' keys (order within the buffer does not matter: sorted next)
-  uint32_t key[EC];
-  int ncand = 0;
-  uint32_t* buf = cbuf[wave];
-  if (!fail) {
-#pragma unroll
-    for (int r = 0; r < E; ++r) {
-      const bool cand = zz[r] > x;          // invisible blocks hold -inf
-      const uint64_t m = __ballot(cand);
-      const int pos = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      if (cand) buf[pos] = score_key(zz[r]);
-      ncand += __popcll(m);
-    }
-#pragma unroll
-    for (int c = 0; c < EC; ++c)
-      if (lane + 64 * c >= ncand) buf[lane + 64 * c] = kPadKey32;
-    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int c = 0; c < EC / 4; ++c) {
-      const uint4 kk = *reinterpret_cast<const uint4*>(buf + EC * lane + 4 * c);
-      key[4 * c] = kk.x; key[4 * c + 1] = kk.y; key[4 * c + 2] = kk.z; key[4 * c + 3] = kk.w;
-    }
-    wave_bitonic_sort32<EC>(key, lane);
-  }
-
-  if (!fail) {
-    bool tie = false;
-#pragma unroll
-    for (int r = 0; r + 1 < EC; ++r) tie |= key[r] == key[r + 1] && key[r] != kPadKey32;
-    const uint32_t next_first = (uint32_t)__shfl_down((int)key[0], 1);
-    tie |= lane < 63 && key[EC - 1] == next_first && key[EC - 1] != kPadKey32;
-    const bool any_tie = __ballot(tie) != 0;
-    uint32_t cut[kMaxLevels];
-#pragma unroll
-    for (int l = 0; l < kMaxLevels; ++l) {
-      const int pos = K[l] - 1;
-      uint32_t v = key[0];
-#pragma unroll
-      for (int r = 1; r < EC; ++r)
-        if (pos >= 0 && pos % EC == r) v = key[r];
-      cut[l] = pos >= 0 ? (uint32_t)__builtin_amdgcn_readlane((int)v, pos / EC) : 0u;
-    }
-    if (any_tie) {
-      int le[kMaxLevels] = {0, 0, 0, 0};
-#pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const bool vis = E * lane + r < nvis;
-        const uint32_t kr = score_key(zz[r]);
-#pragma unroll
-        for (int l = 0; l < kMaxLevels; ++l) le[l] += vis && kr <= cut[l] ? 1 : 0;
-      }
-#pragma unroll
-      for (int l = 0; l < kMaxLevels; ++l)
-        if (l < L && K[l] > 0) fail |= (int)wave_sum((float)le[l]) > K[l];   // exact: counts < 2^24
-    }
-    if (!fail) {
-#pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const int j = E * lane + r;
-        if (j < nvis) {
-          const uint32_t kr = score_key(zz[r]);
-          int lev = -1;
-#pragma unroll
-          for (int l = kMaxLevels - 1; l >= 0; --l)
-            if (l < L && K[l] > 0 && kr <= cut[l]) lev = l;
-          if (64 * j < n_dense_prefix || j >= dfirst) lev = 0;
-          lrow[j] = (int8_t)lev;
-        }
-      }
-    }
-  }
-  if (lane == 0) need_exact[row] = fail ? 1 : 0;
 }
 
 // C * 2^-31 < tau  <=>  C < ceil(tau * 2^31) for an integer mass C (tau * 2^31 is exact in
@@ -1020,24 +754,13 @@ static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
   const int causal = a.causal ? 1 : 0;
   uint8_t* flagged = nullptr;               // exact pass over these rows only (null: every row)
   if (a.cmass == nullptr) {
-    if constexpr (!RANKED) {
-      hipLaunchKernelGGL((block_level_sel_kernel<E>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
-                         a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2], T[3],
-                         a.q_block, a.nqb, causal);
-      if constexpr (E <= 8) return;          // unsettled rows were sorted in the kernel
-      flagged = a.need_exact;
-    } else if constexpr (E > 8) {
-      hipLaunchKernelGGL((block_level_cand_kernel<E>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
-                         a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, frac, a.q_block, a.nqb, causal);
-      flagged = a.need_exact;
-    } else {
-      hipLaunchKernelGGL((block_level_kernel<E, true, 0>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
-                         nullptr, nullptr, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2], T[3], frac,
-                         a.q_block, a.nqb, causal);
-      return;
-    }
+    hipLaunchKernelGGL((block_level_sel_kernel<E, RANKED>), grid, dim3(kMaskThreads), 0, stream, a.z,
+                       a.level_map, a.need_exact, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2],
+                       T[3], frac, a.q_block, a.nqb, causal);
+    if constexpr (E <= 8) return;            // unsettled rows were sorted in the kernel
+    flagged = a.need_exact;
   }
-  hipLaunchKernelGGL((block_level_kernel<E, RANKED, 2>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
+  hipLaunchKernelGGL((block_level_kernel<E, RANKED>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
                      a.cmass, flagged, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2], T[3], frac,
                      a.q_block, a.nqb, causal);
 }
