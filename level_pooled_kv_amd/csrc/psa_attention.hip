@@ -60,6 +60,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   using C = AttnCfg<D, NW>;
   constexpr int RW = NW / KS;                    // waves per 32-key group: row groups of 32 queries
   constexpr int KB = 2 / KS;                     // 32-key halves of a tile each wave computes
+  // d = 64: half the matrix work per exponential, so the softmax's VALU work counts for
+  // more; there the tile max is taken only when a row's sum overflows (the 17776-token
+  // d = 64 layer: 851 -> 817 us; no gain measured at d = 128, also with 64-row blocks)
+  constexpr bool kSkipMax = D == 64;
   constexpr int CPR = C::kCpr, RPB = C::kRpb, BPW = C::kBpw;
   constexpr bool kDirect = sizeof(T) == 2;     // bf16: global -> LDS without registers
   // One LDS object per tile buffer: the wait-count analysis can then tell the direct
@@ -332,40 +336,88 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     }
 
     // online softmax (base 2); this tile's keys all carry bias lvl
-    float tmax = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sacc[kb][x]);
-    {   // lanes l and l^32 hold the two key halves of one query
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float lvlf = (float)lvl;
-    const float mt = fmaf(tmax, cs, lvlf);
-    const bool upd = mt > m_run + 8.0f;
-    if (__ballot(upd)) {
-      // lanes that keep their max scale by 1 (also when it is still -inf after causal masking)
-      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-      l_run *= alpha;
-#pragma unroll
-      for (int tt = 0; tt < C::kDt; ++tt)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) oacc[tt][x] *= alpha;
-      m_run = upd ? mt : m_run;
-    }
-    // a row that has seen no key yet keeps p = 0 (its logits here are all -inf: causal
-    // masking, or with split keys a half tile of only padding rows)
-    const float moff = (KS == 2 || ti.diag) && m_run == -INFINITY ? 0.f : lvlf - m_run;
     bf16x8 preg[2 * KB];
     float lsum = 0.f;
+    const float lvlf = (float)lvl;
+    if constexpr (kSkipMax) {
+      // the exponentials against the running max first; the tile max and a rescale only
+      // where a row's partial sum reached 2^64 or is not a number (scores far above the
+      // running max, or no running max yet), which then recomputes them
+      {
+        const float moff = lvlf - m_run;
 #pragma unroll
-    for (int c = 0; c < 2 * KB; ++c) {
+        for (int c = 0; c < 2 * KB; ++c) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e], cs, moff));
-        lsum += p;
-        preg[c][e] = (__bf16)p;
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e], cs, moff));
+            lsum += p;
+            preg[c][e] = (__bf16)p;
+          }
+        }
+      }
+      if (__ballot(!(lsum < 0x1p64f))) {
+        float tmax = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sacc[kb][x]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+          tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mn = fmaxf(m_run, fmaf(tmax, cs, lvlf));
+        const float alpha = mn == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= alpha;
+#pragma unroll
+        for (int tt = 0; tt < C::kDt; ++tt)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) oacc[tt][x] *= alpha;
+        m_run = mn;
+        const float moff = m_run == -INFINITY ? 0.f : lvlf - m_run;
+        lsum = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2 * KB; ++c) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e], cs, moff));
+            lsum += p;
+            preg[c][e] = (__bf16)p;
+          }
+        }
+      }
+    } else {
+      float tmax = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sacc[kb][x]);
+      {   // lanes l and l^32 hold the two key halves of one query
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float mt = fmaf(tmax, cs, lvlf);
+      const bool upd = mt > m_run + 8.0f;
+      if (__ballot(upd)) {
+        // lanes that keep their max scale by 1 (also when it is still -inf after causal masking)
+        const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int tt = 0; tt < C::kDt; ++tt)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) oacc[tt][x] *= alpha;
+        m_run = upd ? mt : m_run;
+      }
+      // a row that has seen no key yet keeps p = 0 (its logits here are all -inf: causal
+      // masking, or with split keys a half tile of only padding rows)
+      const float moff = (KS == 2 || ti.diag) && m_run == -INFINITY ? 0.f : lvlf - m_run;
+#pragma unroll
+      for (int c = 0; c < 2 * KB; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][8 * (c & 1) + e], cs, moff));
+          lsum += p;
+          preg[c][e] = (__bf16)p;
+        }
       }
     }
     l_run += lsum;
