@@ -424,6 +424,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
       s_ltok[tid] = key_last_token(ok, lvl, prow, N);
     }
   }
+  __syncthreads();                            // s_keyb, s_ltok are read by every wave
 
   const int half = lane >> 5, l32 = lane & 31;
   const int kh = wave & 1, qh = wave >> 1;    // this wave's 32 keys and 32 queries of a 64-row chunk

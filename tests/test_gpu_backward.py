@@ -225,3 +225,28 @@ def test_backward_deterministic(psa):
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("wname", ["cogvx5b", "wan13b"])
+def test_backward_repeatable_full_size(psa, wname):
+    # At full size (thousands of dK/dV workgroups, whose per-key constants are shared
+    # through LDS) three calls give bit-identical gradients: no read of shared state
+    # races its write.
+    w = get_workload(wname)
+    say(f"{w.name}: backward repeatability at full size, generating inputs")
+    q, k, v = generate(w, "q"), generate(w, "k"), generate(w, "v")
+    dO = o.round_to_bf16(np.random.default_rng(11).standard_normal(q.shape).astype(np.float32))
+    prob = psa.Problem(B=w.B, H=w.H, H_kv=w.H_kv, N=w.N, d=w.d, q_block=w.q_block, num_levels=w.num_levels,
+                       dtype=w.dtype)
+    qd, kd, vd, dod = (to_device(x, w.dtype) for x in (q, k, v, dO))
+    kp, vp, kbar = psa.psa_build_pyramid(prob, kd, vd)
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, w.thresholds(), w.n_dense_prefix)
+    out, lse = psa.psa_attention_fwd(prob, qd, kd, vd, kp, vp, lev, want_lse=True)
+    say(f"{w.name}: three GPU backward calls")
+    g1 = psa.psa_attention_bwd(prob, qd, kd, vd, kp, vp, lev, out, lse, dod)
+    for _ in range(2):
+        g2 = psa.psa_attention_bwd(prob, qd, kd, vd, kp, vp, lev, out, lse, dod)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
+            assert torch.equal(a, b), (wname, name, float((a.float() - b.float()).abs().max()))
+    say(f"{w.name}: ok")
