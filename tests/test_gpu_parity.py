@@ -254,6 +254,24 @@ def test_mask_equal_scores_long_rows(psa, N):
     assert np.all(np.diff(grp, axis=-1) >= 0)
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 64), ("f32", 64)])
+def test_mask_long_rows_batched(psa, dtype, d):
+    # More than 512 KV blocks per row (query means and scores in the persistent kernel that
+    # walks groups of 16 query blocks): B = 2, three query heads on one KV head, a ragged
+    # last query block of one row and a ragged last KV block; every row against the oracle.
+    N, L = 36001, 4
+    q, k, v = random_qkv(77, 2, 3, 1, N, d, dtype, scale=2.0)
+    tau = (0.2, 0.45, 0.7, 0.9)
+    ora = o.estimate_mask(q, k, 128, 64, tau, L, 1 / math.sqrt(d))
+    prob = psa.Problem(B=2, H=3, H_kv=1, N=N, d=d, q_block=128, num_levels=L, dtype=dtype)
+    say(f"mask, {prob.nkb} blocks per row, B=2 H=3 H_kv=1 d={d} {dtype}")
+    qd, kd = to_device(q, dtype), to_device(k, dtype)
+    _, _, kbar = psa.psa_build_pyramid(prob, kd, to_device(v, dtype))
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, tau)
+    torch.cuda.synchronize()
+    check_mask(lev.cpu().numpy(), ora, tau, L, 0, label=f"long rows B=2 d={d} {dtype}")
+
+
 def test_deterministic(psa):
     q, k, v = random_qkv(9, 1, 2, 2, 3000, 128, "bf16")
     prob = psa.Problem(B=1, H=2, H_kv=2, N=3000, d=128, q_block=128, num_levels=4, dtype="bf16")
