@@ -157,8 +157,9 @@ psa_status_t psa_apply_similarity_cap(const psa_problem_t* prob, const float* k_
  * thresholds: host array of num_levels floats, nondecreasing, each in [0, 1].
  * cmass_out (nullable): C as float32 [B, H, nqb, nkb].
  * workspace: psa_workspace_bytes(prob, PSA_WS_ESTIMATE_MASK) bytes of device memory
- * (mean queries, then block scores with rows padded to a power of two >= 64, then
- * one flag byte per score row), 16-byte aligned; its contents on entry do not matter.
+ * (mean queries, then block scores with rows padded to the power of two >= max(nkb, 64)
+ * up to nkb = 512 and to a multiple of 256 beyond, then one flag byte per score row),
+ * 16-byte aligned; its contents on entry do not matter.
  * Supported: nkb <= 2048 (N <= 131072).
  */
 psa_status_t psa_estimate_mask(const psa_problem_t* prob, const void* q, const float* k_bar,

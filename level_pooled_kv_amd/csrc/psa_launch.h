@@ -75,8 +75,11 @@ hipError_t launch_pyramid(const PyramidArgs& a, hipStream_t stream);
 hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_similarity_cap(const CapArgs& a, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
-// Padded score-row length of the mask workspace: the smallest power of two >= max(nkb, 64).
+// Padded score-row length of the mask workspace: up to 512 blocks the smallest power of two
+// >= max(nkb, 64); beyond, nkb rounded up to a multiple of 256 (64 lanes x a multiple of 4
+// scores each, so the bucket level pass holds about one score per lane and slot).
 inline int mask_score_stride(int nkb) {
+  if (nkb > 512) return (nkb + 255) / 256 * 256;
   int n = 64;
   while (n < nkb) n <<= 1;
   return n;

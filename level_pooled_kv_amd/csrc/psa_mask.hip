@@ -399,10 +399,9 @@ __device__ __forceinline__ uint32_t wave_exclusive_sum_u32(uint32_t tot, int lan
 template <int E, bool RANKED>
 __global__ void __launch_bounds__(kMaskThreads)
 block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, float* __restrict__ cmass,
-                   uint8_t* __restrict__ need_exact, int N, int nkb, int nrows, int L, int n_dense_prefix,
-                   uint32_t T0, uint32_t T1, uint32_t T2, uint32_t T3, RankFractions frac,
+                   uint8_t* __restrict__ need_exact, int N, int nkb, int zstride, int nrows, int L,
+                   int n_dense_prefix, uint32_t T0, uint32_t T1, uint32_t T2, uint32_t T3, RankFractions frac,
                    int q_block, int nqb, int causal) {
-  constexpr int NP = 64 * E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * (kMaskThreads / 64) + wave;
   if (row >= nrows) return;                 // whole wave; no barrier in this kernel
@@ -416,17 +415,19 @@ block_level_kernel(const float* __restrict__ z, int8_t* __restrict__ level_map, 
     nvis = (min(N, r0 + q_block) - 1) / 64 + 1;
     dfirst = r0 / 64;
   }
-  const float* zr = z + (int64_t)row * NP + E * lane;
+  // the row's scores only (64 E may exceed the row stride; groups of 4 stay in the padded row)
+  const float* zr = z + (int64_t)row * zstride + E * lane;
   float zz[E];
   if constexpr (E >= 4) {
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) {
-      const float4 f = reinterpret_cast<const float4*>(zr)[c];
+      const float4 f = E * lane + 4 * c < nkb ? reinterpret_cast<const float4*>(zr)[c]
+                                              : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       zz[4 * c] = f.x; zz[4 * c + 1] = f.y; zz[4 * c + 2] = f.z; zz[4 * c + 3] = f.w;
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < E; ++r) zz[r] = zr[r];
+    for (int r = 0; r < E; ++r) zz[r] = E * lane + r < nkb ? zr[r] : -INFINITY;
   }
 
   // ---- softmax statistics of the row (the ranked rule needs them only for cmass)
@@ -744,8 +745,11 @@ static uint32_t mass_threshold(float tau) {
   return t <= 0.0 ? 0u : t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
 }
 
+// E: scores per lane of the bucket pass (the score-row stride / 64); the exact pass sorts
+// 64 EP keys, EP the power of two >= E.
 template <int E, bool RANKED>
 static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
+  constexpr int EP = E <= 8 ? E : E <= 16 ? 16 : 32;
   RankFractions frac;
   for (int l = 0; l < kMaxLevels; ++l) frac.f[l] = a.frac[l];
   uint32_t T[kMaxLevels];
@@ -760,9 +764,9 @@ static void launch_level_r(const MaskArgs& a, int nrows, hipStream_t stream) {
     if constexpr (E <= 8) return;            // unsettled rows were sorted in the kernel
     flagged = a.need_exact;
   }
-  hipLaunchKernelGGL((block_level_kernel<E, RANKED>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
-                     a.cmass, flagged, a.N, a.nkb, nrows, a.L, a.n_dense_prefix, T[0], T[1], T[2], T[3], frac,
-                     a.q_block, a.nqb, causal);
+  hipLaunchKernelGGL((block_level_kernel<EP, RANKED>), grid, dim3(kMaskThreads), 0, stream, a.z, a.level_map,
+                     a.cmass, flagged, a.N, a.nkb, mask_score_stride(a.nkb), nrows, a.L, a.n_dense_prefix, T[0],
+                     T[1], T[2], T[3], frac, a.q_block, a.nqb, causal);
 }
 
 template <int E>
@@ -798,7 +802,11 @@ static hipError_t launch_mask_t(const MaskArgs& a, hipStream_t stream) {
     case 128: launch_level_e<2>(a, nrows, stream); break;
     case 256: launch_level_e<4>(a, nrows, stream); break;
     case 512: launch_level_e<8>(a, nrows, stream); break;
+    case 768: launch_level_e<12>(a, nrows, stream); break;
     case 1024: launch_level_e<16>(a, nrows, stream); break;
+    case 1280: launch_level_e<20>(a, nrows, stream); break;
+    case 1536: launch_level_e<24>(a, nrows, stream); break;
+    case 1792: launch_level_e<28>(a, nrows, stream); break;
     case 2048: launch_level_e<32>(a, nrows, stream); break;
     default: return hipErrorInvalidValue;   // nkb above the supported maximum (checked by the ABI layer)
   }

@@ -44,11 +44,18 @@ def test_sizes(psa):
     # mean queries [B,H,nqb,d] + block scores [B,H,nqb,512] (512 KV blocks, already a power of two)
     # + one flag byte per score row
     assert p.workspace_bytes(psa.PSA_WS_ESTIMATE_MASK) == 12 * 256 * 128 * 4 + 12 * 256 * 512 * 4 + 12 * 256
-    # score rows are padded to a power of two >= 64: 278 KV blocks -> 512, 32 -> 64
+    # score rows are padded to a power of two >= 64 up to 512 blocks: 278 KV blocks -> 512,
+    # 32 -> 64; beyond, to a multiple of 256: 1182 -> 1280, 625 -> 768, 2048 -> 2048
     assert (prob(psa, H=48, H_kv=48, N=17776, d=64).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
             == 48 * 139 * 64 * 4 + 48 * 139 * 512 * 4 + 48 * 139)
     assert (prob(psa, H=2, H_kv=2, N=2048, d=64, q_block=64).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
             == 2 * 32 * 64 * 4 + 2 * 32 * 64 * 4 + 2 * 32)
+    assert (prob(psa, H=40, H_kv=40, N=75600).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
+            == 40 * 591 * 128 * 4 + 40 * 591 * 1280 * 4 + 40 * 591)
+    assert (prob(psa, H=1, H_kv=1, N=40000, d=64).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
+            == 313 * 64 * 4 + 313 * 768 * 4 + 313)
+    assert (prob(psa, H=1, H_kv=1, N=64 * 2048).workspace_bytes(psa.PSA_WS_ESTIMATE_MASK)
+            == 1024 * 128 * 4 + 1024 * 2048 * 4 + 1024)
     # backward: lse (base 2) and row dots [B,H,Npad] (N padded to 64 rows), each on a 256-byte
     # boundary, then float32 per-level gradients of K and V [B,H_kv,N+pyramid rows,d]
     r256 = lambda x: (x + 255) // 256 * 256

@@ -272,6 +272,28 @@ def test_mask_long_rows_batched(psa, dtype, d):
     check_mask(lev.cpu().numpy(), ora, tau, L, 0, label=f"long rows B=2 d={d} {dtype}")
 
 
+@pytest.mark.parametrize("N", [89600, 108800, 131072], ids=["1400 blocks", "1700 blocks", "2048 blocks"])
+def test_mask_row_strides(psa, N):
+    # Score rows of 1536, 1792 and 2048 floats (rows past 512 blocks are padded to a
+    # multiple of 256): the bucket pass at 24, 28 and 32 scores per lane and the exact
+    # pass (cumulative mass asked) sorting 2048 keys over the shorter stride.
+    d, L = 64, 4
+    q, k, v = random_qkv(N // 1000 + 3, 1, 1, 1, N, d, "bf16", scale=2.0)
+    tau = (0.1, 0.3, 0.6, 0.85)
+    ora = o.estimate_mask(q, k, 128, 64, tau, L, 1 / math.sqrt(d))
+    prob = psa.Problem(B=1, H=1, H_kv=1, N=N, d=d, q_block=128, num_levels=L, dtype="bf16")
+    say(f"mask, {prob.nkb} blocks per row")
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    _, _, kbar = psa.psa_build_pyramid(prob, kd, to_device(v, "bf16"))
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, tau)
+    lev_c, cm_c = psa.psa_estimate_mask(prob, qd, kbar, tau, want_cmass=True)
+    torch.cuda.synchronize()
+    lev_g = lev.cpu().numpy()
+    check_fast_vs_exact(lev_g, lev_c.cpu().numpy(), to_host(cm_c), tau, L, label=f"N={N}")
+    check_mask(lev_g, ora, tau, L, 0, label=f"N={N}")
+    check_cmass(to_host(cm_c), ora, label=f"N={N}")
+
+
 def test_deterministic(psa):
     q, k, v = random_qkv(9, 1, 2, 2, 3000, 128, "bf16")
     prob = psa.Problem(B=1, H=2, H_kv=2, N=3000, d=128, q_block=128, num_levels=4, dtype="bf16")
