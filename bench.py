@@ -8,10 +8,12 @@ A step is one pass of the whole forward path over one batch of resident inputs:
 psa_build_pyramid, psa_estimate_mask (psa_estimate_mask_ranked with --rule ranked) and
 psa_attention_fwd, enqueued on one stream.
 W untimed steps, then K timed steps bracketed by device synchronisation (the "warm"
-loop: `value` and ms_per_step come from its wall clock); HIP events around every call
-give per-call times (the attention call is a single kernel launch, the roofline's
-kernel). Then K more steps, each after a 512 MiB read that evicts L2 and the MALL (the
-"cold" loop, outside `value`). Per call: mean, median, p10 and p90 of both loops.
+loop: `value` and ms_per_step come from its wall clock), with HIP events around the
+attention call only (a single kernel launch, the roofline's kernel; an event record
+leaves a gap on the stream). Then K untimed steps with events around every call (the
+pyramid's and the mask's per-call times), then K more, each after a 512 MiB read that
+evicts L2 and the MALL (the "cold" loop, outside `value`). Per call: mean, median, p10
+and p90 of the warm and cold loops.
 
 Throughput is effective TFLOP/s: FLOPs of QK^T and PV on the retained pooled rows
 only (sum over retained blocks of 4 * rows * pooled_rows * d), divided by the step
@@ -275,12 +277,13 @@ def main():
     o = torch.empty_like(qd)
 
     def step(ev=None):
-        if ev: ev[0].record()
+        # ev: four events around the three calls (a None entry is not recorded)
+        if ev and ev[0]: ev[0].record()
         if args.similarity is None:
             psa.psa_build_pyramid(prob, kd, vd, k_pyr, v_pyr, k_bar)
         else:
             psa.psa_build_pyramid_sim(prob, kd, vd, k_pyr, v_pyr, k_bar, k_sim)
-        if ev: ev[1].record()
+        if ev and ev[1]: ev[1].record()
         if fractions is None:
             psa.psa_estimate_mask(prob, qd, k_bar, tau, w.n_dense_prefix, level_map=level_map, workspace=ws)
         else:
@@ -288,24 +291,33 @@ def main():
                                          workspace=ws)
         if args.similarity is not None:
             psa.psa_apply_similarity_cap(prob, k_sim, args.similarity, level_map)
-        if ev: ev[2].record()
+        if ev and ev[2]: ev[2].record()
         psa.psa_attention_fwd(prob, qd, kd, vd, k_pyr, v_pyr, level_map, o=o)
-        if ev: ev[3].record()
+        if ev and ev[3]: ev[3].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # warm: K steps back to back (the timed region of `value` and ms_per_step)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # warm: K steps back to back (the timed region of `value` and ms_per_step), with events
+    # around the attention call only (the roofline's live kernel time); every event record
+    # leaves a gap on the stream, so the other calls are timed in a second warm loop
+    att_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(events[s])
+        step([None, None, att_events[s][0], att_events[s][1]])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    attn_warm = np.array([e[0].elapsed_time(e[1]) for e in att_events])            # ms
+    # warm, instrumented: K more steps with events around every call (untimed)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
     per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in events])   # ms
+    per[:, 2] = attn_warm
     pyr_ms, mask_ms, attn_ms = (float(np.mean(per[:, i])) for i in range(3))
     # cold: K more steps, each after reading a 512 MiB buffer (evicts L2 and the 256 MB MALL,
     # so the step's inputs come from HBM). A read leaves only clean lines behind; a write
