@@ -213,12 +213,26 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   // Direct-load path: the byte offsets of tile t's staged rows are computed up front
   // (with the tile's logit corrections when irregular), and the loads themselves are
   // issued one at a time between the S-product MFMAs of the current tile, so no wave stalls
-  // behind a burst of loads queued at the CU's load path.
+  // behind a burst of loads queued at the CU's load path. The tile's descriptor and the
+  // block-list entries of this lane's rows are read from LDS one tile earlier
+  // (prefetch_tile), so forming the offsets waits on no LDS round trip at the start of a
+  // tile.
   struct Stage { const char* kb; const char* vb; uint32_t koff[BPW], voff[BPW]; };
-  auto stage_addr = [&](int t, auto P) {
+  struct Pref { uint32_t desc; int blk[BPW]; };
+  auto prefetch_tile = [&](int t) {
+    Pref pf;
+    pf.desc = __builtin_amdgcn_readfirstlane(tdesc[t]);
+    const TileInfo ti = decode_tile(pf.desc);
+    const int sh = 6 - ti.lvl;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)   // past the valid segments: unused (the row is not ok)
+      pf.blk[i] = (int)blist[ti.base + ((st_row0 + RPB * i) >> sh)];
+    return pf;
+  };
+  auto stage_addr = [&](const Pref& pf, auto P) {
     constexpr int buf = P();
     Stage st;
-    const TileInfo ti = tile_info(t);
+    const TileInfo ti = decode_tile(pf.desc);
     const int lvl = ti.lvl;
     const int sh = 6 - lvl, seglen = 64 >> lvl;
     const int rows_lv = level_rows(lvl);
@@ -232,8 +246,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       const int row = st_row0 + RPB * i;
       const int seg = row >> sh;
       const bool vseg = seg < ti.nseg;
-      const int blk = (int)blist[ti.base + seg];     // unused (row not ok) past the valid segments
-      const int prow = blk * seglen + (row & (seglen - 1));
+      const int prow = pf.blk[i] * seglen + (row & (seglen - 1));
       const bool ok = vseg && prow < rows_lv;
       const int rowel = (ok ? prow : 0) * D;
       st.koff[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ k_swz<D>(row))) * (int)sizeof(T));
@@ -274,6 +287,10 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     issue_tile(0, P0{});
     commit_tile(P0{});
   }
+  // descriptor of the tile being computed, and the prefetched staging of the next one
+  uint32_t dcur = T_total > 0 ? __builtin_amdgcn_readfirstlane(tdesc[0]) : 0u;
+  Pref pf{};
+  if (kDirect && T_total > 0) pf = prefetch_tile(min(1, T_total - 1));
   __syncthreads();
 
   // V operand addressing for ds_read_b64_tr_b16: in 16-lane group G, lane 4m+q points at
@@ -290,15 +307,16 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     // the next tile's staging (past the last tile: a reload of the last tile into the
     // idle buffers, so the interleaved loads need no branch)
     Stage st{};
-    if constexpr (kDirect) st = stage_addr(min(t + 1, T_total - 1), PN{});
+    if constexpr (kDirect) st = stage_addr(pf, PN{});
     else if (t + 1 < T_total) issue_tile(t + 1, PN{});
+    const uint32_t dnext = kDirect ? pf.desc : 0u;
     // the next tile's K and V loads go out one per SK S-product MFMAs, K first: issued
     // early, they have the softmax and the P.V products to land before the tile's wait
     constexpr int SK = KB * C::kQc / (2 * BPW);
     // the compiler's interleaving of LDS reads with the matrix ops of this region
     // (about 1% on the 32760-token layer, interleaved A/B)
     __builtin_amdgcn_iglp_opt(0);
-    const TileInfo ti = tile_info(t);
+    const TileInfo ti = kDirect ? decode_tile(dcur) : tile_info(t);
     const int lvl = ti.lvl;
     const bool irr = ti.irr;
     const uint16_t* Kb = kbuf(P);
@@ -327,6 +345,8 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         }
       }
     }
+    // staging of tile t+2 (the last tile again past the end), read while the S products run
+    if constexpr (kDirect) pf = prefetch_tile(min(t + 2, T_total - 1));
     if (irr) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -450,6 +470,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     }
 
     if (t + 1 < T_total) commit_tile(PN{});
+    if constexpr (kDirect) dcur = dnext;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of tile t+1 have landed
     __syncthreads();
   };
