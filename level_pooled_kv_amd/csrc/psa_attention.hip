@@ -84,7 +84,9 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   __shared__ uint32_t tdesc[kMaxKvBlocks + 4];   // per tile: level | list base << 2 | segs << 16 | irregular << 31
   __shared__ int s_tile[5];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index read as a wave-uniform value: every LDS destination of a direct load is then
+  // formed in scalar registers (no vector-to-scalar moves per load)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
   int bh, qi;
   if (causal && (nqb & 1) == 0) {
@@ -239,6 +241,18 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const int64_t loff = (int64_t)level_off(lvl) * D;
     st.kb = reinterpret_cast<const char*>(lvl == 0 ? kh : kph + loff);
     st.vb = reinterpret_cast<const char*>(lvl == 0 ? vh : vph + loff);
+    if (__builtin_expect(!(ti.irr || ti.diag), 1)) {
+      // a regular tile: every segment is a whole block of full pooled rows, so each staged
+      // row is valid and its byte offset is (pooled row) * row bytes + the chunk's swizzled slot
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int row = st_row0 + RPB * i;
+        const uint32_t rowb = (uint32_t)((pf.blk[i] << sh) + (row & (seglen - 1))) * (uint32_t)(D * sizeof(T));
+        st.koff[i] = rowb + (uint32_t)(8 * (st_pchunk ^ k_swz<D>(row)) * (int)sizeof(T));
+        st.voff[i] = rowb + (uint32_t)(8 * (st_pchunk ^ v_swz<D>(row)) * (int)sizeof(T));
+      }
+      return st;
+    }
     int fx_prow[BPW];
     bool fx_ok[BPW];
 #pragma unroll
@@ -254,7 +268,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       fx_prow[i] = prow;
       fx_ok[i] = ok;
     }
-    if (__builtin_expect(ti.irr || ti.diag, 0)) tile_fixups(ti, buf, fx_prow, fx_ok);
+    tile_fixups(ti, buf, fx_prow, fx_ok);
     return st;
   };
   auto dma_k = [&](const Stage& st, int i, auto P) {
@@ -413,14 +427,16 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         }
       }
     } else {
+      // tile max with the IEEE maximum (v_maximum3_f32), which needs no quieting of its
+      // operands; the scores hold no NaN (masked ones are -inf)
       float tmax = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) tmax = fmaxf(tmax, sacc[kb][x]);
+        for (int x = 0; x < 16; ++x) tmax = __builtin_elementwise_maximum(tmax, sacc[kb][x]);
       {   // lanes l and l^32 hold the two key halves of one query
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-        tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        tmax = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
       const float mt = fmaf(tmax, cs, lvlf);
       const bool upd = mt > m_run + 8.0f;
