@@ -84,7 +84,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
   __shared__ uint32_t tdesc[kMaxKvBlocks + 4];
   __shared__ int s_tile[5];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar LDS destinations
   const int bid = blockIdx.x;
   const int item = (bid & 7) * per_xcd + (bid >> 3);
   if (item >= total_items) return;
@@ -370,7 +370,7 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
   __shared__ float s_keyb[64];
   __shared__ int s_ltok[64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar LDS destinations
   const int bid = blockIdx.x;
   const int item = (bid & 7) * per_xcd + (bid >> 3);
   if (item >= total_items) return;
