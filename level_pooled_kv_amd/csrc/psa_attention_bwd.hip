@@ -475,16 +475,21 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
           constexpr int BPWV = NBLK / 4;             // blocks per wave and tensor
           const int lrow = lane / CH, lch = lane % CH;
           if constexpr (sizeof(T) == 2) {
+            // wave-uniform chunk bases plus 32-bit lane offsets (the scalar-base load form)
+            const char* qc = reinterpret_cast<const char*>(q + (bh * N + r0) * D);
+            const char* oc = reinterpret_cast<const char*>(dout + (bh * N + r0) * D);
+            // an empty asm statement pins each base as one scalar value, so the compiler does not
+            // re-associate the sums into per-lane 64-bit adds
+            asm volatile("" : "+s"(qc), "+s"(oc));
+            const int rlast = N - 1 - r0;                // last valid row of the chunk
 #pragma unroll
             for (int bb = 0; bb < BPWV; ++bb) {
               const int blk = wave * BPWV + bb;
               const int row = blk * RPK + lrow;
-              const int64_t r = min(r0 + row, N - 1);
               const int lc = lch ^ qt_swz<D>(row);     // logical chunk stored in physical slot lch
-              __builtin_amdgcn_global_load_lds((gbl_void*)(q + (bh * N + r) * D + lc * 8), (lds_void*)(Qs + blk * 512),
-                                               16, 0, 0);
-              __builtin_amdgcn_global_load_lds((gbl_void*)(dout + (bh * N + r) * D + lc * 8),
-                                               (lds_void*)(Os + blk * 512), 16, 0, 0);
+              const uint32_t off = (uint32_t)((min(row, rlast) * D + lc * 8) * (int)sizeof(T));
+              __builtin_amdgcn_global_load_lds((gbl_void*)(qc + off), (lds_void*)(Qs + blk * 512), 16, 0, 0);
+              __builtin_amdgcn_global_load_lds((gbl_void*)(oc + off), (lds_void*)(Os + blk * 512), 16, 0, 0);
             }
             if (wave == 0)
               __builtin_amdgcn_global_load_lds((gbl_void*)(lse2p + bh * Npad + r0 + lane), (lds_void*)s_lse2, 4, 0, 0);
@@ -536,22 +541,28 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
         }
         // the 16 query rows of this lane's accumulator entries come in 4 runs of 4
         bf16x8 preg[2], dsreg[2];
+        // causal masking in its own copy of the loop (a scalar branch): the bidirectional
+        // case does no per-pair compares
+        auto probs = [&](auto CAUSAL) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 lse4 = *reinterpret_cast<const float4*>(s_lse2 + 32 * qh + 8 * g4 + 4 * half);
-          const float4 dr4 = *reinterpret_cast<const float4*>(s_D + 32 * qh + 8 * g4 + 4 * half);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 lse4 = *reinterpret_cast<const float4*>(s_lse2 + 32 * qh + 8 * g4 + 4 * half);
+            const float4 dr4 = *reinterpret_cast<const float4*>(s_D + 32 * qh + 8 * g4 + 4 * half);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int x = 4 * g4 + u;
-            const int ql = 32 * qh + 8 * g4 + 4 * half + u;   // query row in the chunk
-            // unseen pairs take an exponent of -inf (p = 0) instead of a branch
-            float arg = fmaf(sacc[x], cs, kbias - (&lse4.x)[u]);
-            if (causal) arg = ktok > r0 + ql ? -INFINITY : arg;
-            const float p = __builtin_amdgcn_exp2f(arg);
-            preg[x >> 3][x & 7] = (__bf16)p;
-            dsreg[x >> 3][x & 7] = (__bf16)(p * (dpacc[x] - (&dr4.x)[u]));
+            for (int u = 0; u < 4; ++u) {
+              const int x = 4 * g4 + u;
+              const int ql = 32 * qh + 8 * g4 + 4 * half + u;   // query row in the chunk
+              // unseen pairs take an exponent of -inf (p = 0) instead of a branch
+              float arg = fmaf(sacc[x], cs, kbias - (&lse4.x)[u]);
+              if constexpr (CAUSAL()) arg = ktok > r0 + ql ? -INFINITY : arg;
+              const float p = __builtin_amdgcn_exp2f(arg);
+              preg[x >> 3][x & 7] = (__bf16)p;
+              dsreg[x >> 3][x & 7] = (__bf16)(p * (dpacc[x] - (&dr4.x)[u]));
+            }
           }
-        }
+        };
+        if (causal) probs(std::true_type{});
+        else probs(std::false_type{});
         // dV^T += dO^T P and dK^T += Q^T dS: A operands read transposed from LDS, the
         // query rows chosen in the order the S accumulator holds them
 #pragma unroll
