@@ -166,30 +166,46 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
     const int64_t loff = (int64_t)level_off(lvl) * D;
     const char* kb = reinterpret_cast<const char*>(lvl == 0 ? kh : kph + loff);
     const char* vb = reinterpret_cast<const char*>(lvl == 0 ? vh : vph + loff);
-    int fx_prow[BPW];
-    bool fx_ok[BPW];
+    uint32_t off[BPW];
+    if (__builtin_expect(!(ti.irr || ti.diag), 1)) {
+      // a regular tile: every segment is a whole block of full pooled rows, so each staged
+      // row is valid (no per-row checks, no fixups)
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int row = st_row0 + RPB * i;
+        const int blk = (int)blist[ti.base + (row >> sh)];
+        off[i] = (uint32_t)((((blk << sh) + (row & (seglen - 1))) * D + 8 * (st_pchunk ^ qt_swz<D>(row))) *
+                            (int)sizeof(T));
+      }
+    } else {
+      int fx_prow[BPW];
+      bool fx_ok[BPW];
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const int row = st_row0 + RPB * i;
+        const int seg = row >> sh;
+        const bool vseg = seg < ti.nseg;
+        const int blk = vseg ? (int)blist[ti.base + seg] : 0;
+        const int prow = blk * seglen + (row & (seglen - 1));
+        const bool ok = vseg && prow < rows_lv;
+        const int rowel = (ok ? prow : 0) * D;
+        off[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ qt_swz<D>(row))) * (int)sizeof(T));
+        fx_prow[i] = prow;
+        fx_ok[i] = ok;
+      }
+      tile_fixups(ti, buf, fx_prow, fx_ok);
+    }
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      const int row = st_row0 + RPB * i;
-      const int seg = row >> sh;
-      const bool vseg = seg < ti.nseg;
-      const int blk = vseg ? (int)blist[ti.base + seg] : 0;
-      const int prow = blk * seglen + (row & (seglen - 1));
-      const bool ok = vseg && prow < rows_lv;
-      const int rowel = (ok ? prow : 0) * D;
-      const uint32_t off = (uint32_t)((rowel + 8 * (st_pchunk ^ qt_swz<D>(row))) * (int)sizeof(T));
       if constexpr (kDirect) {
         const int blkoff = (wave * BPW + i) * 512;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + off), (lds_void*)(kbuf(P) + blkoff), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + off), (lds_void*)(vbuf(P) + blkoff), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + off[i]), (lds_void*)(kbuf(P) + blkoff), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + off[i]), (lds_void*)(vbuf(P) + blkoff), 16, 0, 0);
       } else {
-        fk[i].load(reinterpret_cast<const float*>(kb + off));
-        fv[i].load(reinterpret_cast<const float*>(vb + off));
+        fk[i].load(reinterpret_cast<const float*>(kb + off[i]));
+        fv[i].load(reinterpret_cast<const float*>(vb + off[i]));
       }
-      fx_prow[i] = prow;
-      fx_ok[i] = ok;
     }
-    if (__builtin_expect(ti.irr || ti.diag, 0)) tile_fixups(ti, buf, fx_prow, fx_ok);
   };
   auto commit_tile = [&](auto P) {
     if constexpr (!kDirect) {
@@ -491,10 +507,11 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
               __builtin_amdgcn_global_load_lds((gbl_void*)(qc + off), (lds_void*)(Qs + blk * 512), 16, 0, 0);
               __builtin_amdgcn_global_load_lds((gbl_void*)(oc + off), (lds_void*)(Os + blk * 512), 16, 0, 0);
             }
-            if (wave == 0)
-              __builtin_amdgcn_global_load_lds((gbl_void*)(lse2p + bh * Npad + r0 + lane), (lds_void*)s_lse2, 4, 0, 0);
-            if (wave == 1)
-              __builtin_amdgcn_global_load_lds((gbl_void*)(Dp + bh * Npad + r0 + lane), (lds_void*)s_D, 4, 0, 0);
+            const float* lc0 = lse2p + bh * Npad + r0;
+            const float* dc0 = Dp + bh * Npad + r0;
+            asm volatile("" : "+s"(lc0), "+s"(dc0));
+            if (wave == 0) __builtin_amdgcn_global_load_lds((gbl_void*)(lc0 + lane), (lds_void*)s_lse2, 4, 0, 0);
+            if (wave == 1) __builtin_amdgcn_global_load_lds((gbl_void*)(dc0 + lane), (lds_void*)s_D, 4, 0, 0);
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
           } else {
             Raw8f rq[BPWV], rd[BPWV];
