@@ -31,13 +31,14 @@
 namespace psa {
 
 // ------------------------------------------------------------------ D_r = <dO_r, O_r>
-// Row statistics of the backward, per (b, h) padded to Npad rows (a multiple of 64): the
-// lse in base 2 (+inf for a row that saw no key and for padding, so its P is 0) and D_r
-// (0 on padding).
+// Row statistics of the backward, per (b, h) padded to Npad rows (a multiple of 64), stored
+// as the dK/dV kernel uses them, the starting values of its S and dP accumulators:
+// -lse2 / cs with lse2 the lse in base 2 and cs = scale * log2(e) (-inf for a row that saw
+// no key and for padding, so its P is 0), and -D_r (0 on padding).
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 bwd_rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
-                  float* __restrict__ lse2, float* __restrict__ Dr, int N, int Npad, int64_t rows) {
+                  float* __restrict__ lse2, float* __restrict__ Dr, int N, int Npad, int64_t rows, float cs) {
   constexpr int E = io_traits<T>::per16, CPR = D / E, RPB = 256 / CPR;
   const int t = threadIdx.x, lane = t & 63, chunk = t % CPR;
   const int64_t prow = (int64_t)blockIdx.x * RPB + t / CPR;   // padded row index
@@ -56,8 +57,8 @@ bwd_rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dout, const flo
   s = group_sum<CPR>(s, lane);   // every lane takes part: no early exit above
   if (prow < rows && chunk == 0) {
     const float l = live ? lse[row] : -INFINITY;
-    lse2[prow] = l > -INFINITY ? l * 1.4426950408889634f : INFINITY;
-    Dr[prow] = s;
+    lse2[prow] = l > -INFINITY ? -(l * 1.4426950408889634f) / cs : -INFINITY;
+    Dr[prow] = -s;
   }
 }
 
@@ -126,7 +127,7 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
   const float lse_r = my_row < N ? lse[(int64_t)bh * N + my_row] : -INFINITY;
   const bool live = lse_r > -INFINITY;
   const float lse2 = live ? lse_r * 1.4426950408889634f : 0.f;
-  const float d_r = my_row < N ? Dr[(int64_t)bh * Npad + my_row] : 0.f;
+  const float d_r = my_row < N ? -Dr[(int64_t)bh * Npad + my_row] : 0.f;   // stored negated
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
@@ -542,9 +543,17 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
         if (!active) continue;                // the loop's barrier is at its top: no wave skips one
         // S = Q K^T and dP = dO V^T for 32 queries x 32 keys: lane holds key column krow,
         // rows = queries 32qh + 8(x>>2) + 4half + (x&3)
+        // S starts from -lse2 / cs and dP from -D_r of its query row (the rows of accumulator
+        // entries 4 g4 .. 4 g4 + 3 are 4 consecutive rows), so the exponent below is one FMA
+        // and dS one product
         f32x16 sacc, dpacc;
 #pragma unroll
-        for (int x = 0; x < 16; ++x) sacc[x] = dpacc[x] = 0.f;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(s_lse2 + 32 * qh + 8 * g4 + 4 * half);
+          const float4 d4 = *reinterpret_cast<const float4*>(s_D + 32 * qh + 8 * g4 + 4 * half);
+          sacc[4 * g4] = l4.x; sacc[4 * g4 + 1] = l4.y; sacc[4 * g4 + 2] = l4.z; sacc[4 * g4 + 3] = l4.w;
+          dpacc[4 * g4] = d4.x; dpacc[4 * g4 + 1] = d4.y; dpacc[4 * g4 + 2] = d4.z; dpacc[4 * g4 + 3] = d4.w;
+        }
         const int qrow = 32 * qh + l32;
         const int qswz = qt_swz<D>(qrow), kswz = qt_swz<D>(krow);
 #pragma unroll
@@ -563,18 +572,16 @@ pyramid_attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, c
         auto probs = [&](auto CAUSAL) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const float4 lse4 = *reinterpret_cast<const float4*>(s_lse2 + 32 * qh + 8 * g4 + 4 * half);
-            const float4 dr4 = *reinterpret_cast<const float4*>(s_D + 32 * qh + 8 * g4 + 4 * half);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int x = 4 * g4 + u;
               const int ql = 32 * qh + 8 * g4 + 4 * half + u;   // query row in the chunk
               // unseen pairs take an exponent of -inf (p = 0) instead of a branch
-              float arg = fmaf(sacc[x], cs, kbias - (&lse4.x)[u]);
+              float arg = fmaf(sacc[x], cs, kbias);
               if constexpr (CAUSAL()) arg = ktok > r0 + ql ? -INFINITY : arg;
               const float p = __builtin_amdgcn_exp2f(arg);
               preg[x >> 3][x & 7] = (__bf16)p;
-              dsreg[x >> 3][x & 7] = (__bf16)(p * (dpacc[x] - (&dr4.x)[u]));
+              dsreg[x >> 3][x & 7] = (__bf16)(p * dpacc[x]);
             }
           }
         };
@@ -710,7 +717,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t prows = (int64_t)a.B * a.H * a.Npad;
   const float cs = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3((unsigned)((prows + 256 / CPR - 1) / (256 / CPR))), dim3(256), 0,
-                     stream, o, dout, a.lse, a.lse2, a.Dr, a.N, a.Npad, prows);
+                     stream, o, dout, a.lse, a.lse2, a.Dr, a.N, a.Npad, prows, cs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
