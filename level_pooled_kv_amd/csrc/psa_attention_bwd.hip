@@ -248,21 +248,23 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
     const uint16_t* Vb = vbuf(P);
     int zero;   // opaque: keeps the LDS address arithmetic in the loop (hoisted, it spilled)
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    // lane offsets of the S and dP operand reads (row 32 kb + l32, chunk (2c + half) ^ swz):
+    // the swizzle depends on the row mod 16 only, so the 32-row step kb and the K / V tile
+    // are immediate offsets
+    int ko[C::kQc];
+#pragma unroll
+    for (int c = 0; c < C::kQc; ++c) ko[c] = (l32 + zero) * D + (((2 * c + half) ^ qt_swz<D>(l32)) * 8);
 #pragma unroll
     for (int kbi = 0; kbi < 2 / KS; ++kbi) {
       const int kb = kbi + (2 / KS) * khalf;
       f32x16 sacc, dpacc;
 #pragma unroll
       for (int x = 0; x < 16; ++x) sacc[x] = dpacc[x] = 0.f;
-      const int krow = 32 * kb + l32 + zero;
-      const uint16_t* kr = Kb + krow * D;
-      const uint16_t* vr = Vb + krow * D;
-      const int swz = qt_swz<D>(krow);
 #pragma unroll
       for (int c = 0; c < C::kQc; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((2 * c + half) ^ swz) * 8));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + 32 * kb * D + ko[c]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sacc, 0, 0, 0);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vr + (((2 * c + half) ^ swz) * 8));
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vb + 32 * kb * D + ko[c]);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[c], dpacc, 0, 0, 0);
       }
       if (ti.irr) {
@@ -277,17 +279,27 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
       // dS^T = P^T (dP^T - D), P^T = exp2(cs * S^T + lvl - lse2); keys in the order the
       // transposing K^T reads below deliver them
       bf16x8 dsr[2];
-      const float off = lvlf - lse2;
+      // a row that saw no key takes an offset of -inf, so its P is 0 without a select
+      const float off = live ? lvlf - lse2 : -INFINITY;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int x = 8 * cc + e;
-          const float p = live ? __builtin_amdgcn_exp2f(fmaf(sacc[x], cs, off)) : 0.f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[x], cs, off));
           dsr[cc][e] = (__bf16)(p * (dpacc[x] - d_r));
         }
       }
-      // dq^T += K^T dS^T
+      // dq^T += K^T dS^T. The swizzle of row 16c + 8j + tr_row depends on the row mod 16 only,
+      // so each (j, tt) takes one lane offset and the 16-row step c is an immediate offset
+      int tro[2][C::kDt];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int tt = 0; tt < C::kDt; ++tt) {
+          const int r = 8 * j + tr_row, col = 32 * tt + tr_col;
+          tro[j][tt] = (r + zero) * D + ((col >> 3) ^ qt_swz<D>(r)) * 8 + (col & 7);
+        }
 #pragma unroll
       for (int tt = 0; tt < C::kDt; ++tt) {
 #pragma unroll
@@ -295,12 +307,8 @@ pyramid_attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k, con
           const int c = 2 * kb + cc;
           bf16x4 part[2];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int row = 16 * c + 8 * j + tr_row + zero;
-            const int col = 32 * tt + tr_col;
-            const int chunk = (col >> 3) ^ qt_swz<D>(row);
-            part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Kb + row * D + chunk * 8 + (col & 7)));
-          }
+          for (int j = 0; j < 2; ++j)
+            part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Kb + tro[j][tt] + 16 * c * D));
           const bf16x8 a = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
           dqacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsr[cc], dqacc[tt], 0, 0, 0);
         }
