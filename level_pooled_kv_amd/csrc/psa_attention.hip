@@ -215,20 +215,33 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   // Direct-load path: the byte offsets of tile t's staged rows are computed up front
   // (with the tile's logit corrections when irregular), and the loads themselves are
   // issued one at a time between the S-product MFMAs of the current tile, so no wave stalls
-  // behind a burst of loads queued at the CU's load path. The tile's descriptor and the
-  // block-list entries of this lane's rows are read from LDS one tile earlier
+  // behind a burst of loads queued at the CU's load path. A wave stages 16 consecutive rows
+  // of a tile, 16 w + q_i with q_i = RPB i + lane / CPR; its rows with q_i < 8 and those with
+  // q_i >= 8 each lie in one segment (segments are 8 rows or more), so the block index of
+  // every staged row is wave-uniform: one for the lower and one for the upper 8 rows. The
+  // tile's descriptor and these two block indices are read from LDS one tile earlier
   // (prefetch_tile), so forming the offsets waits on no LDS round trip at the start of a
-  // tile.
+  // tile; a regular tile's row offset is then a scalar term plus the lane's own part (q_i
+  // rows and the swizzled chunk slot), which is the same for every tile.
+  static_assert(RPB * BPW == 16, "a wave stages 16 consecutive rows");
+  constexpr int RB = D * (int)sizeof(T);          // bytes per K or V row
+  uint32_t ck[BPW], cv[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int q = RPB * i + lane / CPR;
+    ck[i] = (uint32_t)(q * RB + 8 * (st_pchunk ^ k_swz<D>(16 * wave + q)) * (int)sizeof(T));
+    cv[i] = (uint32_t)(q * RB + 8 * (st_pchunk ^ v_swz<D>(16 * wave + q)) * (int)sizeof(T));
+  }
   struct Stage { const char* kb; const char* vb; uint32_t koff[BPW], voff[BPW]; };
-  struct Pref { uint32_t desc; int blk[BPW]; };
+  struct Pref { uint32_t desc; int blk[2]; };
   auto prefetch_tile = [&](int t) {
     Pref pf;
     pf.desc = __builtin_amdgcn_readfirstlane(tdesc[t]);
     const TileInfo ti = decode_tile(pf.desc);
     const int sh = 6 - ti.lvl;
-#pragma unroll
-    for (int i = 0; i < BPW; ++i)   // past the valid segments: unused (the row is not ok)
-      pf.blk[i] = (int)blist[ti.base + ((st_row0 + RPB * i) >> sh)];
+    // past the valid segments: unused (the rows are not ok)
+    pf.blk[0] = __builtin_amdgcn_readfirstlane((int)blist[ti.base + ((16 * wave) >> sh)]);
+    pf.blk[1] = __builtin_amdgcn_readfirstlane((int)blist[ti.base + ((16 * wave + 8) >> sh)]);
     return pf;
   };
   auto stage_addr = [&](const Pref& pf, auto P) {
@@ -243,13 +256,17 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     st.vb = reinterpret_cast<const char*>(lvl == 0 ? vh : vph + loff);
     if (__builtin_expect(!(ti.irr || ti.diag), 1)) {
       // a regular tile: every segment is a whole block of full pooled rows, so each staged
-      // row is valid and its byte offset is (pooled row) * row bytes + the chunk's swizzled slot
+      // row is valid; pooled row of staged row i = U_u + q_i for its half u, with
+      // U_u = (block << sh) + ((16 w + 8 u) mod seglen) - 8 u (wave-uniform). Unsigned
+      // arithmetic: U_u * RB may wrap below zero, the sum with the lane part does not.
+      uint32_t ub[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        ub[u] = (uint32_t)((pf.blk[u] << sh) + ((16 * wave + 8 * u) & (seglen - 1)) - 8 * u) * (uint32_t)RB;
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
-        const int row = st_row0 + RPB * i;
-        const uint32_t rowb = (uint32_t)((pf.blk[i] << sh) + (row & (seglen - 1))) * (uint32_t)(D * sizeof(T));
-        st.koff[i] = rowb + (uint32_t)(8 * (st_pchunk ^ k_swz<D>(row)) * (int)sizeof(T));
-        st.voff[i] = rowb + (uint32_t)(8 * (st_pchunk ^ v_swz<D>(row)) * (int)sizeof(T));
+        st.koff[i] = ub[RPB * i >= 8 ? 1 : 0] + ck[i];
+        st.voff[i] = ub[RPB * i >= 8 ? 1 : 0] + cv[i];
       }
       return st;
     }
@@ -260,7 +277,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       const int row = st_row0 + RPB * i;
       const int seg = row >> sh;
       const bool vseg = seg < ti.nseg;
-      const int prow = pf.blk[i] * seglen + (row & (seglen - 1));
+      const int prow = pf.blk[RPB * i >= 8 ? 1 : 0] * seglen + (row & (seglen - 1));
       const bool ok = vseg && prow < rows_lv;
       const int rowel = (ok ? prow : 0) * D;
       st.koff[i] = (uint32_t)((rowel + 8 * (st_pchunk ^ k_swz<D>(row))) * (int)sizeof(T));
@@ -313,6 +330,11 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   const int trg = lane >> 4, trs = lane & 15;
   const int tr_row = 4 * (trg >> 1) + (trs >> 2);
   const int tr_col = 16 * (trg & 1) + 4 * (trs & 3);
+  // byte offset of the K operand read of chunk c: row l32 of the key half, 16-byte chunk
+  // (2c + half) ^ swizzle
+  int kro[C::kQc];
+#pragma unroll
+  for (int c = 0; c < C::kQc; ++c) kro[c] = (l32 * D + (((2 * c + half) ^ k_swz<D>(l32)) * 8)) * 2;   // bytes
 
   // tile t (t % 2 == P()): prefetch tile t+1 into the other buffers, then compute t
   auto body = [&](int t, auto P) {
@@ -336,18 +358,21 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     const uint16_t* Kb = kbuf(P);
     const uint16_t* Vb = vbuf(P);
 
-    // S^T = K Q^T: the wave's 32-key halves (kb + KB khalf of the tile)
+    // S^T = K Q^T: the wave's 32-key halves (kb + KB khalf of the tile). The lane offsets of
+    // the K operand reads do not change from tile to tile (the swizzle depends on the row mod
+    // 16 only; the key half and the buffer are immediate offsets); an empty asm statement
+    // keeps them in registers instead of recomputing them every tile.
+#pragma unroll
+    for (int c = 0; c < C::kQc; ++c) asm volatile("" : "+v"(kro[c]));
     f32x16 sacc[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int x = 0; x < 16; ++x) sacc[kb][x] = 0.f;
-      const int krow = 32 * (kb + KB * khalf) + l32;
-      const uint16_t* kr_l = Kb + krow * D;
-      const int swz = k_swz<D>(krow);
+      const uint16_t* kr_l = Kb + 32 * (kb + KB * khalf) * D;
 #pragma unroll
       for (int c = 0; c < C::kQc; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr_l + (((2 * c + half) ^ swz) * 8));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kr_l) + kro[c]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sacc[kb], 0, 0, 0);
         if constexpr (kDirect) {
           const int j = kb * C::kQc + c;
@@ -452,7 +477,8 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
       }
       // a row that has seen no key yet keeps p = 0 (its logits here are all -inf: causal
       // masking, or with split keys a half tile of only padding rows)
-      const float moff = (KS == 2 || ti.diag) && m_run == -INFINITY ? 0.f : lvlf - m_run;
+      float moff = lvlf - m_run;
+      if (KS == 2 || ti.diag) moff = m_run == -INFINITY ? 0.f : moff;
 #pragma unroll
       for (int c = 0; c < 2 * KB; ++c) {
 #pragma unroll
