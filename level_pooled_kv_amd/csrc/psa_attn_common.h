@@ -85,13 +85,25 @@ __device__ __forceinline__ void build_tile_lists(const int8_t* __restrict__ lrow
                                                  int diag_from, int16_t* blist, uint32_t* tdesc,
                                                  int* s_tile) {
   const int lane = threadIdx.x & 63;
-  int cnt[4] = {0, 0, 0, 0};
-  for (int j0 = 0; j0 < nkb; j0 += 64) {
-    const int j = j0 + lane;
-    int lev = j < nkb ? (int)lrow[j] : -1;
-    if (lev >= L) lev = -1;
+  // the row's levels, one entry per lane and 64-entry round, loaded once with every load
+  // in flight before any is used (a load per round waited for in turn costs a memory
+  // latency per round, twice)
+  constexpr int KR = kMaxKvBlocks / 64;
+  int lv[KR];
 #pragma unroll
-    for (int l = 0; l < 4; ++l) cnt[l] += __popcll(__ballot(lev == l));
+  for (int k = 0; k < KR; ++k) {
+    const int j = 64 * k + lane;
+    lv[k] = j < nkb ? (int)lrow[j] : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < KR; ++k)
+    if (lv[k] >= L) lv[k] = -1;
+  int cnt[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    if (64 * k >= nkb) break;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) cnt[l] += __popcll(__ballot(lv[k] == l));
   }
   int pos[4];
   pos[0] = 0;
@@ -106,10 +118,11 @@ __device__ __forceinline__ void build_tile_lists(const int8_t* __restrict__ lrow
 #pragma unroll
     for (int l = 0; l < 5; ++l) s_tile[l] = tfirst[l];
   }
-  for (int j0 = 0; j0 < nkb; j0 += 64) {
-    const int j = j0 + lane;
-    int lev = j < nkb ? (int)lrow[j] : -1;
-    if (lev >= L) lev = -1;
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    if (64 * k >= nkb) break;
+    const int j = 64 * k + lane;
+    const int lev = lv[k];
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       const uint64_t m = __ballot(lev == l);
