@@ -556,7 +556,39 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (my_row < N && khalf == 0) {
+  if constexpr (sizeof(T) == 2) {
+    // bf16: a wave's 32 output rows go through LDS (the idle tile buffers, 16-byte chunks
+    // XOR-swizzled by row) and leave as whole rows, four 256-byte rows per 16-byte store
+    // instruction, instead of 8-byte pieces of 32 rows per instruction
+    constexpr int CH = D / 8;                   // 16-byte chunks per row
+    uint16_t* ost = KS == 1 ? (wave == 0 ? K0 : wave == 1 ? K1 : wave == 2 ? V0 : V1)
+                            : (wave % RW == 0 ? V0 : V1);   // the key-half merge used K0, K1
+    if (khalf == 0) {
+#pragma unroll
+      for (int tt = 0; tt < C::kDt; ++tt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int pc = (4 * tt + g4) ^ (l32 & (CH - 1));
+          const float y0 = oacc[tt][4 * g4] * inv, y1 = oacc[tt][4 * g4 + 1] * inv;
+          const float y2 = oacc[tt][4 * g4 + 2] * inv, y3 = oacc[tt][4 * g4 + 3] * inv;
+          *reinterpret_cast<uint2*>(ost + l32 * D + pc * 8 + 4 * half) =
+              make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+        }
+      }
+    }
+    __syncthreads();
+    if (khalf == 0) {
+      const int rbase = q0 + 32 * (KS == 1 ? wave : wave % RW);
+      T* obase = o + ((int64_t)bh * N + rbase) * D;
+#pragma unroll
+      for (int i = 0; i < 32 * CH / 64; ++i) {
+        const int idx = 64 * i + lane, r = idx / CH, c = idx % CH;
+        if (rbase + r < N) st128(obase + r * D + c * 8, ld128(ost + r * D + ((c ^ (r & (CH - 1))) * 8)));
+      }
+      if (lse && half == 0 && my_row < N)
+        lse[(int64_t)bh * N + my_row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    }
+  } else if (my_row < N && khalf == 0) {
     T* orow = o + ((int64_t)bh * N + my_row) * D;
 #pragma unroll
     for (int tt = 0; tt < C::kDt; ++tt) {
@@ -565,11 +597,7 @@ pyramid_attn_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         const int d = 32 * tt + 8 * g4 + 4 * half;
         const float y0 = oacc[tt][4 * g4] * inv, y1 = oacc[tt][4 * g4 + 1] * inv;
         const float y2 = oacc[tt][4 * g4 + 2] * inv, y3 = oacc[tt][4 * g4 + 3] * inv;
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<uint2*>(orow + d) = make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
-        } else {
-          *reinterpret_cast<float4*>(orow + d) = make_float4(y0, y1, y2, y3);
-        }
+        *reinterpret_cast<float4*>(orow + d) = make_float4(y0, y1, y2, y3);
       }
     }
     if (lse && half == 0)
