@@ -158,6 +158,8 @@ block_score_kernel(const float* __restrict__ qbar, const float* __restrict__ kba
   const int row = qt * 32 + l32;
   if (row >= nqb) return;
   float* zr = z + ((int64_t)bh * nqb + row) * zstride;
+  // ln n_j: every block but the last holds min(64, N) tokens
+  const float ln_full = logf((float)min(64, N)), ln_last = logf((float)(N - 64 * (nkb - 1)));
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
     const int j0 = kt * 32 + 8 * g4 + 4 * half;
@@ -165,8 +167,7 @@ block_score_kernel(const float* __restrict__ qbar, const float* __restrict__ kba
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int j = j0 + x;
-      const float lnn = logf((float)min(64, N - 64 * j));
-      out[x] = fmaf(scale, acc[4 * g4 + x], lnn);
+      out[x] = fmaf(scale, acc[4 * g4 + x], j == nkb - 1 ? ln_last : ln_full);
     }
     if (j0 + 3 < nkb) {
       *reinterpret_cast<float4*>(zr + j0) = make_float4(out[0], out[1], out[2], out[3]);
@@ -256,12 +257,14 @@ qblock_score_kernel(const T* __restrict__ q, const float* __restrict__ kbar, flo
   const int n = lane & 15, kq = lane >> 4;
   const float* qcol = qs + n * QS + 4 * kq;
   float* zr = z + ((int64_t)bh * nqb + i0 + n) * zstride;
+  // ln n_j: every block but the last holds min(64, N) tokens
+  const float ln_full = logf((float)min(64, N)), ln_last = logf((float)(N - 64 * (nkb - 1)));
   auto store = [&](int tile, const f32x4& acc) {
     if (n >= nrow || tile >= ntiles) return;
     const int j0 = tile * 16 + 4 * kq;
     float out[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) out[x] = fmaf(scale, acc[x], logf((float)min(64, N - 64 * (j0 + x))));
+    for (int x = 0; x < 4; ++x) out[x] = fmaf(scale, acc[x], j0 + x == nkb - 1 ? ln_last : ln_full);
     if (j0 + 3 < nkb) {
       *reinterpret_cast<float4*>(zr + j0) = make_float4(out[0], out[1], out[2], out[3]);
     } else {
