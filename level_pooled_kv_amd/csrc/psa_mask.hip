@@ -590,14 +590,24 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
   int8_t* lrow = level_map + (int64_t)row * nkb;
   // softmax statistics in block_level_kernel's grouping, so every mass is the same float
   float mx = -INFINITY, zmin = INFINITY;
+  const bool full = nvis == nkb;            // no causal cut in this row (the same in every lane)
+  if (full) {
 #pragma unroll
-  for (int r = 0; r < E; ++r) {
-    const int j = E * lane + r;
-    if (j < nvis) {
-      mx = fmaxf(mx, zz[r]);
-      zmin = fminf(zmin, zz[r]);
-    } else if (j < nkb) {
-      lrow[j] = -1;                         // causal: blocks after the query block
+    for (int r = 0; r < E; ++r) {
+      const bool in = E * lane + r < nkb;
+      mx = fmaxf(mx, in ? zz[r] : -INFINITY);
+      zmin = fminf(zmin, in ? zz[r] : INFINITY);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const int j = E * lane + r;
+      if (j < nvis) {
+        mx = fmaxf(mx, zz[r]);
+        zmin = fminf(zmin, zz[r]);
+      } else if (j < nkb) {
+        lrow[j] = -1;                       // causal: blocks after the query block
+      }
     }
   }
   mx = wave_max(mx);
@@ -720,17 +730,38 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
       const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(ck[0] >> 32), last);
       kap[l] = ((uint64_t)hi << 32) | lo;
     }
-#pragma unroll
-    for (int r = 0; r < E; ++r) {
+    auto level_at = [&](int r) {
       const int j = E * lane + r;
-      if (j < nvis) {
-        const uint64_t kr = rank_key(zz[r], j);
-        int lev = -1;
+      const uint64_t kr = rank_key(zz[r], j);
+      int lev = -1;
 #pragma unroll
-        for (int l = kMaxLevels - 1; l >= 0; --l)
-          if (has[l] && kr <= kap[l]) lev = l;
-        if (64 * j < n_dense_prefix || j >= dfirst) lev = 0;
-        lrow[j] = (int8_t)lev;
+      for (int l = kMaxLevels - 1; l >= 0; --l)
+        if (has[l] && kr <= kap[l]) lev = l;
+      if (64 * j < n_dense_prefix || j >= dfirst) lev = 0;
+      return lev;
+    };
+    bool done = false;
+    if constexpr (E % 4 == 0) {
+      // every group of four whole and 4-byte aligned (the caller's map may start anywhere)
+      if (full && (nkb & 3) == 0 && (reinterpret_cast<uintptr_t>(level_map) & 3) == 0) {
+#pragma unroll
+        for (int c = 0; c < E / 4; ++c) {
+          const int j0 = E * lane + 4 * c;
+          if (j0 < nkb) {
+            const uint32_t w4 = (uint32_t)(level_at(4 * c) & 0xff) | (uint32_t)(level_at(4 * c + 1) & 0xff) << 8 |
+                                (uint32_t)(level_at(4 * c + 2) & 0xff) << 16 |
+                                (uint32_t)(level_at(4 * c + 3) & 0xff) << 24;
+            *reinterpret_cast<uint32_t*>(lrow + j0) = w4;
+          }
+        }
+        done = true;
+      }
+    }
+    if (!done) {
+#pragma unroll
+      for (int r = 0; r < E; ++r) {
+        const int j = E * lane + r;
+        if (j < nvis) lrow[j] = (int8_t)level_at(r);
       }
     }
   }
