@@ -742,8 +742,9 @@ block_level_sel_kernel(const float* __restrict__ z, int8_t* __restrict__ level_m
     };
     bool done = false;
     if constexpr (E % 4 == 0) {
-      // every group of four whole and 4-byte aligned (the caller's map may start anywhere)
-      if (full && (nkb & 3) == 0 && (reinterpret_cast<uintptr_t>(level_map) & 3) == 0) {
+      // every group of four whole; the map itself is 16-byte aligned (the library checks it),
+      // so each group's 4-byte store is aligned
+      if (full && (nkb & 3) == 0) {
 #pragma unroll
         for (int c = 0; c < E / 4; ++c) {
           const int j0 = E * lane + 4 * c;

@@ -198,6 +198,35 @@ def test_mask_equal_scores(psa):
     check_mask(lev.cpu().numpy(), ora["mask"], tau, 4, 0, label="equal scores")
 
 
+@pytest.mark.parametrize("N,causal", [(16384, False), (32768, False), (16384, True)],
+                         ids=["256 blocks", "512 blocks", "256 blocks causal"])
+def test_mask_level_map_in_buffer(psa, N, causal):
+    # The level pass stores four levels with one 4-byte store where the row length is a
+    # multiple of 4 (else one byte per level). A map placed 16 bytes into a larger buffer
+    # must get the same levels as a map of its own and as the exact pass, with no byte
+    # around it changed; a map that is not 16-byte aligned is refused before any kernel
+    # runs (its bytes, which overlap the first map, stay as they were).
+    q, k, v = random_qkv(N // 1000 + 40, 1, 2, 2, N, 64, "bf16")
+    tau = (0.05, 0.2, 0.4, 0.6)
+    prob = psa.Problem(B=1, H=2, H_kv=2, N=N, d=64, q_block=128, num_levels=4, dtype="bf16", causal=causal)
+    say(f"level map inside a larger buffer: N={N} causal={causal}")
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    _, _, kbar = psa.psa_build_pyramid(prob, kd, to_device(v, "bf16"))
+    lev, _ = psa.psa_estimate_mask(prob, qd, kbar, tau)
+    n, shape = lev.numel(), tuple(lev.shape)
+    buf = torch.full((n + 48,), 99, dtype=torch.int8, device=lev.device)
+    lev_o = buf[16:16 + n].view(shape)
+    assert lev_o.data_ptr() % 16 == 0
+    psa.psa_estimate_mask(prob, qd, kbar, tau, level_map=lev_o)
+    with pytest.raises(psa.PsaError, match="aligned"):
+        psa.psa_estimate_mask(prob, qd, kbar, tau, level_map=buf[1:1 + n].view(shape))
+    lev_c, _ = psa.psa_estimate_mask(prob, qd, kbar, tau, want_cmass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lev, lev_o), "map inside a larger buffer"
+    assert torch.equal(lev, lev_c), "exact pass"
+    assert bool((buf[:16] == 99).all()) and bool((buf[16 + n:] == 99).all()), "bytes outside the map"
+
+
 @pytest.mark.parametrize("N,tau", [(4096, (0.05, 0.2, 0.4, 0.6)), (30000, (0.02, 0.08, 0.2, 0.5))],
                          ids=["64 blocks", "469 blocks"])
 def test_mask_equal_scores_split_by_cut(psa, N, tau):
